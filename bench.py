@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the differential-attention hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+  lambda   diffattn_lambda for the prefill heads
+  prefill  diffattn_prefill on prefill_v1: V1 form, B 2, H 16, N 4096,
+           d_qk 64, d_v 128, causal, bf16, RMSNorm epilogue
+  lambda   diffattn_lambda for the decode heads
+  decode   diffattn_decode on decode_v2: V2 form, 64 sequences, context
+           U{8192..32768}, 8 KV heads, 64 query heads, d 128, page 64, bf16
+Inputs are resident in HBM before the timed region. Each call is bracketed by
+HIP events on the stream the library launches on, so per-kernel averages come
+from the same timed steps.
+
+Output: one JSON line. ``value`` is prefill throughput, FLOPs counted as
+B*H*(N^2/2)*2*(2*d_qk + 2*d_v) (both branches, QK and PV, causal pairs
+halved), over the mean time of the lambda + prefill part of a step; the
+``decode`` object gives the decode part's algorithmic HBM bytes (every
+visible token's K and V once, plus Q, output and page-table entries) per
+second. ``roofline`` is the prefill kernel against the bf16 dense MFMA peak,
+``decode.roofline`` the decode call against HBM bandwidth. ``cpu_baseline``
+times the fp64 CPU oracle on a bounded random sample of prefill rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(B, H, N, dqk, dv):
+    return B * H * (N * N / 2.0) * 2.0 * (2 * dqk + 2 * dv)
+
+
+def decode_bytes(d):
+    L = d.ctx_len.astype(np.int64)
+    kv = int(L.sum()) * d.H_kv * (d.d_qk + d.d_v) * 2
+    q = d.B * 2 * d.H * d.d_qk * 2
+    out = d.B * d.H * d.d_v * 2
+    table = int(((L + d.page - 1) // d.page).sum()) * 4 + d.B * 4
+    return kv + q + out + table
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "differential_attention_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        e = t.get(name)
+        if e and e.get("source_hash") == kernel_source_hash():
+            return e.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def cpu_baseline(p, lam64, budget_s):
+    """Oracle FLOP/s on a random sample of prefill rows (same inputs)."""
+    import oracle
+    rng = np.random.default_rng(1234)
+    q1, q2, k1, k2, v = (p.f32(n) for n in ("q1", "q2", "k1", "k2", "v"))
+    per_key = 2 * (2 * p.d_qk + 2 * p.d_v)
+
+    def run(nrows):
+        rows = rng.choice(p.B * p.H * p.N, size=nrows, replace=False).astype(np.int64)
+        flops = float(((rows % p.N) + 1).sum()) * per_key
+        t0 = time.perf_counter()
+        oracle.prefill(q1, q2, k1, k2, v, lam64, depth=p.depth, causal=True, norm=True,
+                       gamma=p.gamma, eps=p.eps, rows=rows)
+        return flops, time.perf_counter() - t0
+
+    f0, t0 = run(64)                      # calibration
+    n = int(min(p.B * p.H * p.N, max(64, 64 * budget_s / max(t0, 1e-3))))
+    f, t = run(n)
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} random query rows of prefill_v1 (of {p.B * p.H * p.N}), fp64, "
+                      f"{t:.1f} s, FLOPs counted per visible key as for the GPU"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="profiling aid: run only one part of the step")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(sharding is by (batch, KV head) with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import differential_attention_amd as da
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if not os.path.exists(da.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_gen = time.perf_counter()
+    p = W.prefill_v1()
+    d = W.decode_v2() if args.only != "prefill" else None
+    log(f"inputs generated in {time.perf_counter() - t_gen:.1f} s")
+
+    # prefill tensors
+    P = {n: to_dev(getattr(p, n)) for n in ("q1", "q2", "k1", "k2", "v")}
+    lamv_p = [torch.from_numpy(x).to(dev) for x in (p.lam_q1, p.lam_k1, p.lam_q2, p.lam_k2)]
+    gamma = torch.from_numpy(p.gamma).to(dev)
+    out_p = torch.empty((p.B, p.H, p.N, p.d_v), dtype=torch.bfloat16, device=dev)
+    lam_p = torch.empty(p.H, dtype=torch.float32, device=dev)
+    # decode tensors
+    if d is not None:
+        qd = to_dev(d.q_full)
+        kc, vc = to_dev(d.k1_cache), to_dev(d.v_cache)
+        table = torch.from_numpy(d.page_table).to(dev)
+        ctx = torch.from_numpy(d.ctx_len).to(dev)
+        lamv_d = [torch.from_numpy(x).to(dev) for x in (d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2)]
+        lam_d = torch.empty(d.H, dtype=torch.float32, device=dev)
+        out_d = torch.empty((d.B, d.H, d.d_v), dtype=torch.bfloat16, device=dev)
+        ws_bytes = da.decode_workspace_bytes(qd[:, 0::2], qd[:, 1::2], kc, vc, table, ctx, lam_d,
+                                             depth=d.depth)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(ev):
+        if args.only != "decode":
+            ev[0].record(stream)
+            da.lambda_(*lamv_p, p.depth, out=lam_p)
+            ev[1].record(stream)
+            da.prefill(P["q1"], P["q2"], P["k1"], P["k2"], P["v"], lam_p, depth=p.depth, causal=True,
+                       norm=True, gamma=gamma, eps=p.eps, out=out_p)
+            ev[2].record(stream)
+        if d is not None:
+            ev[3].record(stream)
+            da.lambda_(*lamv_d, d.depth, out=lam_d)
+            ev[4].record(stream)
+            da.decode(qd[:, 0::2], qd[:, 1::2], kc, vc, table, ctx, lam_d, depth=d.depth, out=out_d,
+                      workspace=ws)
+            ev[5].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    for e in evs:
+        step(e)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = t_start.elapsed_time(t_end)
+
+    def mean_ms(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+
+    res = {}
+    F = prefill_flops(p.B, p.H, p.N, p.d_qk, p.d_v)
+    if args.only != "decode":
+        pre_part = mean_ms(0, 2)
+        pre_kernel = mean_ms(1, 2)
+        res["prefill_part_ms"] = pre_part
+        res["prefill_kernel_ms"] = pre_kernel
+        log(f"prefill: step part {pre_part * 1e3:.1f} us, kernel {pre_kernel * 1e3:.1f} us, "
+            f"{F / pre_kernel / 1e9:.1f} TFLOP/s")
+    if d is not None:
+        dbytes = decode_bytes(d)
+        dec_part = mean_ms(3, 5)
+        dec_call = mean_ms(4, 5)
+        res["decode_part_ms"] = dec_part
+        res["decode_call_ms"] = dec_call
+        log(f"decode: step part {dec_part * 1e3:.1f} us, call {dec_call * 1e3:.1f} us, "
+            f"{dbytes / dec_call / 1e6:.1f} GB/s")
+
+    line = {
+        "metric": "prefill TFLOP/s (% bf16 MFMA peak) + decode GB/s (% HBM peak), 1 MI355X",
+        "value": None, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill_v1 (V1, B 2, H 16, N 4096, d_qk 64, d_v 128, causal, RMS) + "
+                               "decode_v2 (V2 paged, 64 seqs, ctx U{8192..32768}, 8 KV / 64 Q heads, "
+                               "d 128, page 64)",
+                   "global_batch": p.B, "seq_len": p.N, "parallelism": "none (1 GPU)"},
+        "wall_s": wall,
+    }
+    if args.only != "decode":
+        line["value"] = F / (res["prefill_part_ms"] * 1e-3) / 1e12
+        ach = F / (res["prefill_kernel_ms"] * 1e-3) / 1e12
+        line["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<64,false,true>",
+                            "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": ach / BF16_PEAK_TFLOPS, "traffic": load_traffic("prefill_v1")}
+    if d is not None:
+        gbs = dbytes / (res["decode_part_ms"] * 1e-3) / 1e9
+        ach = dbytes / (res["decode_call_ms"] * 1e-3) / 1e9
+        line["decode"] = {"value": gbs, "unit": "GB/s", "tokens_per_s": d.B / (res["decode_part_ms"] * 1e-3),
+                          "bytes_per_step": dbytes,
+                          "roofline": {"bound": "hbm", "kernel": "decode_split_kernel + decode_combine_kernel",
+                                       "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic("decode_v2")}}
+    if not args.no_cpu and args.only != "decode":
+        import oracle
+        lam64 = oracle.lambda_(p.lam_q1, p.lam_k1, p.lam_q2, p.lam_k2, p.depth)
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(p, lam64, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,270 @@
+"""Python binding of libdiffattn (differential attention on MI355X / gfx950).
+
+A thin ctypes layer over the C ABI declared in ``include/diffattn.h``: it
+turns torch tensors into pointers, sizes and element strides, passes torch's
+current HIP stream, and raises on a non-zero status. Every step of the
+computation runs in the library's HIP kernels; torch only owns device memory
+and the stream. There is no fallback: if ``libdiffattn.so`` is missing, or no
+GPU is visible, the calls raise.
+
+Functions (same names as the C entry points, without the prefix):
+  lambda_init(depth)                             -> float (host)
+  lambda_(lq1, lk1, lq2, lk2, depth)             -> [H] fp32 device tensor
+  prefill(q1, q2, k1, k2, v, lam, ...)           -> [B, H, N, d_v]
+  decode_workspace_bytes(...)                    -> int
+  decode(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, ...) -> [B, H, d_v]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdiffattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+NORM_NONE, NORM_RMS = 0, 1
+
+_c_int64_3 = ctypes.c_int64 * 3
+_c_int64_2 = ctypes.c_int64 * 2
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("H_kv", ctypes.c_int), ("N", ctypes.c_int),
+        ("d_qk", ctypes.c_int), ("d_v", ctypes.c_int),
+        ("q1", ctypes.c_void_p), ("q2", ctypes.c_void_p),
+        ("k1", ctypes.c_void_p), ("k2", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("sq1", _c_int64_3), ("sq2", _c_int64_3), ("sk1", _c_int64_3), ("sk2", _c_int64_3),
+        ("sv", _c_int64_3),
+        ("lambda_", ctypes.c_void_p),
+        ("depth", ctypes.c_int),
+        ("causal", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("norm", ctypes.c_int),
+        ("gamma", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+        ("so", _c_int64_3),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("H_kv", ctypes.c_int),
+        ("d_qk", ctypes.c_int), ("d_v", ctypes.c_int), ("page_size", ctypes.c_int),
+        ("max_pages", ctypes.c_int), ("num_pages", ctypes.c_int),
+        ("q1", ctypes.c_void_p), ("q2", ctypes.c_void_p),
+        ("sq1", _c_int64_2), ("sq2", _c_int64_2),
+        ("k1_cache", ctypes.c_void_p), ("k2_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("ctx_len", ctypes.c_void_p),
+        ("lambda_", ctypes.c_void_p),
+        ("depth", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("norm", ctypes.c_int),
+        ("gamma", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+        ("so", _c_int64_2),
+        ("split_pages", ctypes.c_int),
+        ("dev_err", ctypes.c_void_p),
+    ]
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libdiffattn error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libdiffattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m differential_attention_amd.build`")
+    lib = ctypes.CDLL(p)
+    V, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.diffattn_lambda_init.argtypes = [I]
+    lib.diffattn_lambda_init.restype = ctypes.c_double
+    lib.diffattn_lambda.argtypes = [V, V, V, V, I, I, I, V, V]
+    lib.diffattn_lambda.restype = I
+    lib.diffattn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), V]
+    lib.diffattn_prefill.restype = I
+    lib.diffattn_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
+    lib.diffattn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.diffattn_decode.argtypes = [ctypes.POINTER(DecodeArgs), V, ctypes.c_size_t, V]
+    lib.diffattn_decode.restype = I
+    lib.diffattn_last_error.argtypes = []
+    lib.diffattn_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        msg = load_library().diffattn_last_error().decode()
+        raise DiffAttnError(rc, msg)
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def lambda_init(depth: int) -> float:
+    """lambda_init(depth) = 0.8 - 0.6 exp(-0.3 (depth - 1)) (host, fp64)."""
+    return float(load_library().diffattn_lambda_init(int(depth)))
+
+
+def lambda_(lq1, lk1, lq2, lk2, depth: int, out=None, stream=None):
+    """Per-head lambda [H] (fp32, device) from four [H, d_lambda] fp32 device tensors."""
+    import torch
+    vecs = [x.contiguous() for x in (lq1, lk1, lq2, lk2)]
+    H, dl = vecs[0].shape
+    for x in vecs:
+        if x.shape != (H, dl) or x.dtype != torch.float32 or not x.is_cuda:
+            raise ValueError("lambda vectors must be [H, d_lambda] fp32 device tensors of one shape")
+    if out is None:
+        out = torch.empty(H, dtype=torch.float32, device=vecs[0].device)
+    rc = load_library().diffattn_lambda(*(_ptr(x) for x in vecs), H, dl, int(depth), _ptr(out),
+                                        _stream(stream))
+    _check(rc)
+    return out
+
+
+def _strides3(t):
+    s = t.stride()
+    if t.dim() != 4 or s[3] != 1:
+        raise ValueError("expected a 4-d tensor with unit innermost stride")
+    return (s[0], s[1], s[2])
+
+
+def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool = True, norm: bool = False,
+            gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, stream=None):
+    """Differential-attention prefill.
+
+    q1, q2 [B, H, N, d_qk]; k1, k2 [B, H_kv, N, d_qk] (pass the same tensor
+    for both in the V2 form); v [B, H_kv, N, d_v]; lam [H] fp32 device;
+    gamma [H, d_v] fp32 device when norm (V1). Views with unit innermost
+    stride are accepted as they are. Returns out [B, H, N, d_v]."""
+    import torch
+    B, H, N, dqk = q1.shape
+    Hkv, dv = k1.shape[1], v.shape[3]
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q1.dtype, device=q1.device)
+    a = PrefillArgs()
+    a.dtype = _dtype_code(q1)
+    for t in (q2, k1, k2, v, out):
+        if t.dtype != q1.dtype:
+            raise TypeError("all tensors must share one dtype")
+    a.B, a.H, a.H_kv, a.N, a.d_qk, a.d_v = B, H, Hkv, N, dqk, dv
+    a.q1, a.q2, a.k1, a.k2, a.v = _ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v)
+    a.sq1, a.sq2 = _c_int64_3(*_strides3(q1)), _c_int64_3(*_strides3(q2))
+    a.sk1, a.sk2 = _c_int64_3(*_strides3(k1)), _c_int64_3(*_strides3(k2))
+    a.sv, a.so = _c_int64_3(*_strides3(v)), _c_int64_3(*_strides3(out))
+    if lam.dtype != torch.float32 or lam.numel() != H:
+        raise ValueError("lam must be an fp32 tensor of H elements")
+    a.lambda_ = _ptr(lam)
+    a.depth = int(depth)
+    a.causal = int(bool(causal))
+    a.scale = float(scale)
+    a.norm = NORM_RMS if norm else NORM_NONE
+    a.gamma = _ptr(gamma) if norm else None
+    a.eps = float(eps)
+    a.out = _ptr(out)
+    _check(load_library().diffattn_prefill(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
+                 scale, out, split_pages, dev_err, k2_cache=None) -> DecodeArgs:
+    B, H, dqk = q1.shape
+    P, Hkv, page, _ = k_cache.shape
+    dv = v_cache.shape[3]
+    a = DecodeArgs()
+    a.dtype = _dtype_code(q1)
+    a.B, a.H, a.H_kv, a.d_qk, a.d_v = B, H, Hkv, dqk, dv
+    a.page_size, a.max_pages, a.num_pages = page, page_table.shape[1], P
+    a.q1, a.q2 = _ptr(q1), _ptr(q2)
+    if q1.stride(2) != 1 or q2.stride(2) != 1:
+        raise ValueError("q1/q2 need unit innermost stride")
+    a.sq1 = _c_int64_2(q1.stride(0), q1.stride(1))
+    a.sq2 = _c_int64_2(q2.stride(0), q2.stride(1))
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    a.k1_cache = _ptr(k_cache)
+    a.k2_cache = _ptr(k2_cache if k2_cache is not None else k_cache)
+    a.v_cache = _ptr(v_cache)
+    if not (page_table.is_contiguous() and ctx_len.is_contiguous()):
+        raise ValueError("page_table and ctx_len must be contiguous int32 tensors")
+    a.page_table = _ptr(page_table)
+    a.ctx_len = _ptr(ctx_len)
+    a.lambda_ = _ptr(lam)
+    a.depth = int(depth)
+    a.scale = float(scale)
+    a.norm = NORM_RMS if norm else NORM_NONE
+    a.gamma = _ptr(gamma) if norm else None
+    a.eps = float(eps)
+    a.out = _ptr(out) if out is not None else None
+    a.so = _c_int64_2(out.stride(0), out.stride(1)) if out is not None else _c_int64_2(H * dv, dv)
+    a.split_pages = int(split_pages)
+    a.dev_err = _ptr(dev_err)
+    return a
+
+
+def decode_workspace_bytes(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int,
+                           norm: bool = False, gamma=None, eps: float = 1e-5, scale: float = 0.0,
+                           split_pages: int = 0) -> int:
+    a = _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
+                     scale, None, split_pages, None)
+    return int(load_library().diffattn_decode_workspace_bytes(ctypes.byref(a)))
+
+
+def decode(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int, norm: bool = False,
+           gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, workspace=None,
+           split_pages: int = 0, dev_err=None, stream=None):
+    """Paged decode (one query token per sequence).
+
+    q1, q2 [B, H, d]; k_cache, v_cache [num_pages, H_kv, page, d] contiguous
+    (one key cache serves both branches); page_table [B, max_pages] int32;
+    ctx_len [B] int32; lam [H] fp32. Returns out [B, H, d_v]."""
+    import torch
+    B, H, _ = q1.shape
+    dv = v_cache.shape[3]
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q1.dtype, device=q1.device)
+    a = _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
+                     scale, out, split_pages, dev_err)
+    lib = load_library()
+    need = int(lib.diffattn_decode_workspace_bytes(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q1.device)
+    _check(lib.diffattn_decode(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

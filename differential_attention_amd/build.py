@@ -1,0 +1,78 @@
+"""Build libdiffattn.so (gfx950) in-tree with hipcc.
+
+    python -m differential_attention_amd.build
+
+Every HIP translation unit is compiled for gfx950 only. Packed-fp32 VALU ops
+are disabled in device code (-packed-fp32-ops); hipcc's host pass warns that
+it does not know that feature, which is harmless.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libdiffattn.so")
+
+HIP_SOURCES = ["lambda.hip", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip"]
+HOST_SOURCES = ["api.cpp"]      # host code that calls the HIP runtime
+PLAIN_SOURCES = ["plan.cpp"]    # host code with no HIP dependency
+
+ARCH = "gfx950"
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l and l.strip())
+    if r.returncode != 0:
+        raise RuntimeError("command failed: " + " ".join(cmd) + "\n" + out)
+    return out
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every source and link libdiffattn.so. Always recompiles."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    common = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall"]
+    cmds = []
+    objs = []
+    for s in HIP_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        cmds.append([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS, *common, "-c",
+                     os.path.join(CSRC, s), "-o", o])
+        objs.append(o)
+    for s in HOST_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        cmds.append([hipcc, *common, "-c", os.path.join(CSRC, s), "-o", o])
+        objs.append(o)
+    for s in PLAIN_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        cmds.append(["g++", *common, "-c", os.path.join(CSRC, s), "-o", o])
+        objs.append(o)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for out in ex.map(_run, cmds):
+            if verbose and out:
+                print(out)
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

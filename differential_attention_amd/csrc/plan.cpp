@@ -1,0 +1,259 @@
+// plan.cpp -- host-only argument validation and launch planning (no HIP).
+#include "plan.hpp"
+
+#include <math.h>
+
+#include <algorithm>
+#include <vector>
+
+namespace da {
+
+double lambda_init(int depth) {
+    if (depth < 1) return NAN;
+    return 0.8 - 0.6 * exp(-0.3 * (double)(depth - 1));
+}
+
+namespace {
+
+int fail(std::string *msg, int code, const std::string &text) {
+    if (msg) *msg = text;
+    return code;
+}
+
+// A strided tensor: byte extent [lo, hi) and whether its elements are distinct.
+struct Extent {
+    uintptr_t lo = 0, hi = 0;
+};
+
+struct Dim {
+    int64_t size, stride;
+};
+
+// Byte extent of a tensor with the given dims (element strides, all >= 0).
+bool extent_of(const void *p, size_t elem, const std::vector<Dim> &dims, Extent *e) {
+    int64_t last = 0;
+    for (const Dim &d : dims) {
+        if (d.size <= 0) return false;
+        if (d.stride < 0) return false;
+        if (d.stride > 0 && (d.size - 1) > INT64_MAX / d.stride) return false;
+        last += (d.size - 1) * d.stride;
+        if (last < 0) return false;
+    }
+    e->lo = (uintptr_t)p;
+    e->hi = e->lo + (uintptr_t)(last + 1) * elem;
+    return true;
+}
+
+// True when no two index tuples map to the same element: after sorting the
+// non-trivial dims by stride, each stride covers the span of the smaller ones.
+bool non_overlapping(std::vector<Dim> dims) {
+    dims.erase(std::remove_if(dims.begin(), dims.end(), [](const Dim &d) { return d.size == 1; }),
+               dims.end());
+    std::sort(dims.begin(), dims.end(), [](const Dim &a, const Dim &b) { return a.stride < b.stride; });
+    int64_t span = 1;  // elements covered by the dims seen so far
+    for (const Dim &d : dims) {
+        if (d.stride < span) return false;
+        span = d.stride * (d.size - 1) + span;
+    }
+    return true;
+}
+
+bool overlaps(const Extent &a, const Extent &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+int check_lambda(const float *lq1, const float *lk1, const float *lq2, const float *lk2, int H,
+                 int d_lambda, int depth, const float *out, std::string *msg) {
+    if (H < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda: H must be >= 1");
+    if (d_lambda < 1 || d_lambda > 4096)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda: d_lambda must be in [1, 4096]");
+    if (depth < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda: depth must be >= 1");
+    if (!lq1 || !lk1 || !lq2 || !lk2 || !out)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda: null pointer");
+    const void *ins[4] = {lq1, lk1, lq2, lk2};
+    for (const void *p : ins)
+        if (!aligned(p, 4)) return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda: misaligned input");
+    if (!aligned(out, 4)) return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda: misaligned output");
+    Extent eo{(uintptr_t)out, (uintptr_t)out + (uintptr_t)H * 4};
+    for (const void *p : ins) {
+        Extent ei{(uintptr_t)p, (uintptr_t)p + (uintptr_t)H * d_lambda * 4};
+        if (overlaps(eo, ei))
+            return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda: output overlaps an input");
+    }
+    return DIFFATTN_OK;
+}
+
+int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string *msg) {
+    *plan = PrefillPlan();
+    if (!a) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: null argument struct");
+    if (a->dtype != DIFFATTN_BF16 && a->dtype != DIFFATTN_F32)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: unknown dtype");
+    if (a->B < 0 || a->N < 0) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: B and N must be >= 0");
+    if (a->H < 1 || a->H_kv < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: H and H_kv must be >= 1");
+    if (a->H % a->H_kv != 0)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: H must be a multiple of H_kv");
+    if (a->d_qk < 1 || a->d_v < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: d_qk and d_v must be >= 1");
+    if (a->depth < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: depth must be >= 1");
+    if (a->causal != 0 && a->causal != 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: causal must be 0 or 1");
+    if (a->norm != DIFFATTN_NORM_NONE && a->norm != DIFFATTN_NORM_RMS)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: unknown norm");
+    if (!(a->scale >= 0.0f) || isinf(a->scale))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: scale must be finite and >= 0");
+    if (a->norm == DIFFATTN_NORM_RMS && !(a->eps > 0.0f && !isinf(a->eps)))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: eps must be finite and > 0");
+
+    if (a->dtype == DIFFATTN_BF16) {
+        bool ok = (a->d_qk == 64 && a->d_v == 128) || (a->d_qk == 128 && a->d_v == 128);
+        if (!ok)
+            return fail(msg, DIFFATTN_EUNSUPPORTED,
+                        "diffattn_prefill: bf16 supports (d_qk, d_v) = (64, 128) or (128, 128)");
+        plan->kind = PrefillKind::Bf16;
+    } else {
+        if (a->d_qk > 128 || a->d_v > 128)
+            return fail(msg, DIFFATTN_EUNSUPPORTED, "diffattn_prefill: f32 supports d_qk, d_v <= 128");
+        plan->kind = PrefillKind::F32;
+    }
+    if (a->B == 0 || a->N == 0) {
+        plan->empty = true;
+        return DIFFATTN_OK;
+    }
+    if (!a->q1 || !a->q2 || !a->k1 || !a->k2 || !a->v || !a->lambda || !a->out)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: null tensor pointer");
+    if (a->norm == DIFFATTN_NORM_RMS && !a->gamma)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: RMS norm needs gamma");
+
+    const size_t elem = a->dtype == DIFFATTN_BF16 ? 2 : 4;
+    const size_t align = a->dtype == DIFFATTN_BF16 ? 16 : 4;
+    const int64_t smul = a->dtype == DIFFATTN_BF16 ? 8 : 1;
+    struct T {
+        const char *name;
+        const void *p;
+        const int64_t *s;
+        int64_t h, d;
+    } ts[6] = {{"q1", a->q1, a->sq1, a->H, a->d_qk},   {"q2", a->q2, a->sq2, a->H, a->d_qk},
+               {"k1", a->k1, a->sk1, a->H_kv, a->d_qk}, {"k2", a->k2, a->sk2, a->H_kv, a->d_qk},
+               {"v", a->v, a->sv, a->H_kv, a->d_v},     {"out", a->out, a->so, a->H, a->d_v}};
+    Extent ext[6];
+    for (int i = 0; i < 6; ++i) {
+        const T &t = ts[i];
+        for (int k = 0; k < 3; ++k)
+            if (t.s[k] < 0 || t.s[k] % smul != 0)
+                return fail(msg, DIFFATTN_EINVAL,
+                            std::string("diffattn_prefill: stride of ") + t.name +
+                                (a->dtype == DIFFATTN_BF16 ? " must be a non-negative multiple of 8"
+                                                           : " must be non-negative"));
+        if (!aligned(t.p, align))
+            return fail(msg, DIFFATTN_EINVAL, std::string("diffattn_prefill: ") + t.name + " is misaligned");
+        std::vector<Dim> dims = {{a->B, t.s[0]}, {t.h, t.s[1]}, {a->N, t.s[2]}, {t.d, 1}};
+        if (!extent_of(t.p, elem, dims, &ext[i]))
+            return fail(msg, DIFFATTN_EINVAL, std::string("diffattn_prefill: bad strides for ") + t.name);
+        if (i == 5 && !non_overlapping(dims))
+            return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: out has overlapping elements");
+    }
+    if (!aligned(a->lambda, 4) || (a->gamma && a->norm == DIFFATTN_NORM_RMS && !aligned(a->gamma, 4)))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: lambda/gamma misaligned");
+    Extent lam{(uintptr_t)a->lambda, (uintptr_t)a->lambda + (uintptr_t)a->H * 4};
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(ext[5], ext[i]))
+            return fail(msg, DIFFATTN_EINVAL, std::string("diffattn_prefill: out overlaps ") + ts[i].name);
+    if (overlaps(ext[5], lam)) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: out overlaps lambda");
+    if (a->norm == DIFFATTN_NORM_RMS) {
+        Extent g{(uintptr_t)a->gamma, (uintptr_t)a->gamma + (uintptr_t)a->H * a->d_v * 4};
+        if (overlaps(ext[5], g)) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: out overlaps gamma");
+    }
+    plan->shared_k = a->k1 == a->k2 && a->sk1[0] == a->sk2[0] && a->sk1[1] == a->sk2[1] &&
+                     a->sk1[2] == a->sk2[2];
+    return DIFFATTN_OK;
+}
+
+int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *msg) {
+    *plan = DecodePlan();
+    if (!a) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: null argument struct");
+    if (a->dtype != DIFFATTN_BF16 && a->dtype != DIFFATTN_F32)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: unknown dtype");
+    if (a->B < 0) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: B must be >= 0");
+    if (a->H < 1 || a->H_kv < 1 || a->H % a->H_kv != 0)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: need H >= 1, H_kv >= 1, H % H_kv == 0");
+    if (a->d_qk < 1 || a->d_v < 1 || a->page_size < 1 || a->max_pages < 1 || a->num_pages < 1)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: sizes must be >= 1");
+    if (a->depth < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: depth must be >= 1");
+    if (a->norm != DIFFATTN_NORM_NONE && a->norm != DIFFATTN_NORM_RMS)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: unknown norm");
+    if (!(a->scale >= 0.0f) || isinf(a->scale))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: scale must be finite and >= 0");
+    if (a->norm == DIFFATTN_NORM_RMS && !(a->eps > 0.0f && !isinf(a->eps)))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: eps must be finite and > 0");
+    if (a->split_pages < 0) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: split_pages must be >= 0");
+    if ((int64_t)a->max_pages * a->page_size > (1 << 30))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: max_pages * page_size too large");
+    if (a->dtype != DIFFATTN_BF16 || a->d_qk != 128 || a->d_v != 128 || a->page_size != 64)
+        return fail(msg, DIFFATTN_EUNSUPPORTED,
+                    "diffattn_decode: supports bf16 with d_qk = d_v = 128 and page_size 64");
+    const int group = a->H / a->H_kv;
+    if (group > 8)
+        return fail(msg, DIFFATTN_EUNSUPPORTED, "diffattn_decode: at most 8 output heads per KV head");
+    if (a->k1_cache != a->k2_cache)
+        return fail(msg, DIFFATTN_EUNSUPPORTED, "diffattn_decode: the branches must share the key cache");
+
+    // plan: enough (sequence, KV head, split) items to fill the chip several times over
+    const int64_t units = (int64_t)(a->B > 0 ? a->B : 1) * a->H_kv;
+    int sp = a->split_pages;
+    if (sp == 0) {
+        int64_t want = (8192 + units - 1) / units;
+        want = std::max<int64_t>(1, std::min<int64_t>(want, a->max_pages));
+        sp = (int)((a->max_pages + want - 1) / want);
+        sp = std::max(sp, 8);  // at least 512 tokens per item
+    }
+    sp = std::min(sp, a->max_pages);
+    plan->split_pages = sp;
+    plan->num_splits = (a->max_pages + sp - 1) / sp;
+    plan->qrows = 2 * group;
+    plan->ws_bytes = (size_t)(a->B > 0 ? a->B : 0) * a->H_kv * plan->num_splits * plan->qrows *
+                     (size_t)(a->d_v + 2) * sizeof(float);
+
+    if (a->B == 0) return DIFFATTN_OK;
+    if (!a->q1 || !a->q2 || !a->k1_cache || !a->v_cache || !a->page_table || !a->ctx_len ||
+        !a->lambda || !a->out)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: null pointer");
+    if (a->norm == DIFFATTN_NORM_RMS && !a->gamma)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: RMS norm needs gamma");
+    const int64_t strides[6] = {a->sq1[0], a->sq1[1], a->sq2[0], a->sq2[1], a->so[0], a->so[1]};
+    for (int64_t s : strides)
+        if (s < 0 || s % 8 != 0)
+            return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: strides must be non-negative multiples of 8");
+    const void *al16[] = {a->q1, a->q2, a->k1_cache, a->v_cache, a->out};
+    for (const void *p : al16)
+        if (!aligned(p, 16)) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: tensor not 16-byte aligned");
+    if (!aligned(a->page_table, 4) || !aligned(a->ctx_len, 4) || !aligned(a->lambda, 4))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: int/float array misaligned");
+    Extent eo, e;
+    std::vector<Dim> od = {{a->B, a->so[0]}, {a->H, a->so[1]}, {a->d_v, 1}};
+    if (!extent_of(a->out, 2, od, &eo) || !non_overlapping(od))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: bad output strides");
+    const int64_t kv_elems = (int64_t)a->num_pages * a->H_kv * a->page_size;
+    struct R {
+        const void *p;
+        size_t bytes;
+    } rs[] = {{a->k1_cache, (size_t)kv_elems * a->d_qk * 2},
+              {a->v_cache, (size_t)kv_elems * a->d_v * 2},
+              {a->page_table, (size_t)a->B * a->max_pages * 4},
+              {a->ctx_len, (size_t)a->B * 4},
+              {a->lambda, (size_t)a->H * 4}};
+    for (const R &r : rs) {
+        e.lo = (uintptr_t)r.p;
+        e.hi = e.lo + r.bytes;
+        if (overlaps(eo, e)) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: out overlaps an input");
+    }
+    const void *qs[2] = {a->q1, a->q2};
+    const int64_t *qstr[2] = {a->sq1, a->sq2};
+    for (int i = 0; i < 2; ++i) {
+        std::vector<Dim> qd = {{a->B, qstr[i][0]}, {a->H, qstr[i][1]}, {a->d_qk, 1}};
+        if (!extent_of(qs[i], 2, qd, &e)) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: bad q strides");
+        if (overlaps(eo, e)) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: out overlaps q");
+    }
+    return DIFFATTN_OK;
+}
+
+}  // namespace da

@@ -1,0 +1,202 @@
+"""The C ABI on the CPU: the library loads, exports every function declared in
+include/diffattn.h, and rejects bad arguments on the host before any launch.
+No call here reaches a kernel (this container has no GPU)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import differential_attention_amd as da
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(da.LIB_PATH):
+        from differential_attention_amd import build
+        build.build()
+    return da.load_library()
+
+
+def _declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(diffattn_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"diffattn_prefill", "diffattn_decode", "diffattn_lambda"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """ctypes mirrors of the argument structs have the C compiler's layout."""
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "diffattn.h"', "int main(void) {"]
+    for cname, py in (("diffattn_prefill_args", da.PrefillArgs), ("diffattn_decode_args", da.DecodeArgs)):
+        src.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            cf = "lambda" if fname == "lambda_" else fname
+            src.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {cf}));')
+    src.append("return 0; }")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)])
+    out = subprocess.check_output([str(exe)], text=True).split("\n")
+    pys = {"diffattn_prefill_args": da.PrefillArgs, "diffattn_decode_args": da.DecodeArgs}
+    for line in filter(None, out):
+        cname, field, value = line.split()
+        py = pys[cname]
+        got = ctypes.sizeof(py) if field == "size" else getattr(py, field).offset
+        assert got == int(value), (cname, field)
+
+
+def test_lambda_init_matches_oracle(lib):
+    for d in (1, 2, 12, 20, 100):
+        assert abs(da.lambda_init(d) - oracle.lambda_init(d)) <= 1e-15
+    assert math.isnan(da.lambda_init(0))
+
+
+FAKE = 0x7F0000000000  # a 256-aligned fake device address; never dereferenced
+
+
+def _prefill_args(**kw):
+    a = da.PrefillArgs()
+    a.dtype = da.BF16
+    a.B, a.H, a.H_kv, a.N, a.d_qk, a.d_v = 1, 4, 2, 128, 64, 128
+    step = 1 << 24
+    a.q1, a.q2, a.k1, a.k2, a.v = FAKE, FAKE + step, FAKE + 2 * step, FAKE + 3 * step, FAKE + 4 * step
+    for f, d in (("sq1", 64), ("sq2", 64), ("sk1", 64), ("sk2", 64), ("sv", 128)):
+        h = 4 if f.startswith("sq") else 2
+        setattr(a, f, (ctypes.c_int64 * 3)(h * 128 * d, 128 * d, d))
+    a.lambda_ = FAKE + 5 * step
+    a.depth, a.causal, a.scale, a.norm = 1, 1, 0.0, da.NORM_RMS
+    a.gamma = FAKE + 6 * step
+    a.eps = 1e-5
+    a.out = FAKE + 7 * step
+    a.so = (ctypes.c_int64 * 3)(4 * 128 * 128, 128 * 128, 128)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _rc(lib, a):
+    return lib.diffattn_prefill(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("H", 3, da.EINVAL),                 # H % H_kv != 0
+    ("H_kv", 0, da.EINVAL),
+    ("N", -1, da.EINVAL),
+    ("depth", 0, da.EINVAL),
+    ("causal", 2, da.EINVAL),
+    ("norm", 7, da.EINVAL),
+    ("dtype", 9, da.EINVAL),
+    ("eps", 0.0, da.EINVAL),
+    ("scale", -1.0, da.EINVAL),
+    ("d_qk", 96, da.EUNSUPPORTED),       # no bf16 kernel for (96, 128)
+    ("q1", None, da.EINVAL),
+    ("gamma", None, da.EINVAL),          # RMS without gamma
+    ("k1", FAKE + 2 * (1 << 24) + 2, da.EINVAL),   # misaligned bf16 pointer
+])
+def test_prefill_rejects(lib, field, value, code):
+    a = _prefill_args(**{field: value})
+    assert _rc(lib, a) == code
+    assert lib.diffattn_last_error().decode().startswith("diffattn_prefill")
+
+
+def test_prefill_rejects_bad_strides_and_alias(lib):
+    a = _prefill_args(sq1=(ctypes.c_int64 * 3)(4 * 128 * 64, 128 * 64, 60))   # not a multiple of 8
+    assert _rc(lib, a) == da.EINVAL
+    a = _prefill_args(out=FAKE)  # out overlaps q1
+    assert _rc(lib, a) == da.EINVAL
+    assert "overlaps" in lib.diffattn_last_error().decode()
+    a = _prefill_args(so=(ctypes.c_int64 * 3)(4 * 128 * 128, 128 * 128, 64))  # rows overlap
+    assert _rc(lib, a) == da.EINVAL
+
+
+def test_prefill_f32_size_limits(lib):
+    a = _prefill_args(dtype=da.F32, d_qk=129)
+    assert _rc(lib, a) == da.EUNSUPPORTED
+
+
+def test_empty_prefill_is_a_no_op(lib):
+    a = _prefill_args(N=0, q1=None, q2=None, k1=None, k2=None, v=None, out=None)
+    assert _rc(lib, a) == da.OK
+
+
+def _decode_args(**kw):
+    a = da.DecodeArgs()
+    a.dtype = da.BF16
+    a.B, a.H, a.H_kv, a.d_qk, a.d_v = 64, 32, 8, 128, 128
+    a.page_size, a.max_pages, a.num_pages = 64, 512, 20000
+    step = 1 << 34
+    a.q1, a.q2 = FAKE, FAKE + 256
+    a.sq1 = (ctypes.c_int64 * 2)(64 * 128, 256)
+    a.sq2 = (ctypes.c_int64 * 2)(64 * 128, 256)
+    a.k1_cache = a.k2_cache = FAKE + step
+    a.v_cache = FAKE + 2 * step
+    a.page_table = FAKE + 3 * step
+    a.ctx_len = FAKE + 3 * step + (1 << 20)
+    a.lambda_ = FAKE + 3 * step + (2 << 20)
+    a.depth, a.scale, a.norm, a.gamma, a.eps = 20, 0.0, da.NORM_NONE, None, 1e-5
+    a.out = FAKE + 3 * step + (3 << 20)
+    a.so = (ctypes.c_int64 * 2)(32 * 128, 128)
+    a.split_pages = 0
+    a.dev_err = None
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_workspace_and_plan(lib):
+    a = _decode_args()
+    ws = lib.diffattn_decode_workspace_bytes(ctypes.byref(a))
+    # 64 sequences x 8 KV heads x splits x 8 query rows x (128 + 2) floats
+    per_split = 64 * 8 * 8 * 130 * 4
+    assert ws > 0 and ws % per_split == 0
+    splits = ws // per_split
+    assert 2 <= splits <= 512
+    a = _decode_args(split_pages=64)
+    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == 8 * per_split
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d_qk", 64, da.EUNSUPPORTED),
+    ("page_size", 32, da.EUNSUPPORTED),
+    ("dtype", da.F32, da.EUNSUPPORTED),
+    ("H", 40, da.EINVAL),               # not a multiple of H_kv
+    ("k2_cache", FAKE + 5 * (1 << 34), da.EUNSUPPORTED),
+    ("page_table", None, da.EINVAL),
+    ("split_pages", -1, da.EINVAL),
+    ("out", FAKE, da.EINVAL),           # overlaps q1
+])
+def test_decode_rejects(lib, field, value, code):
+    a = _decode_args(**{field: value})
+    assert lib.diffattn_decode(ctypes.byref(a), FAKE + 6 * (1 << 34), 1 << 40, None) == code
+
+
+def test_decode_rejects_small_workspace(lib):
+    a = _decode_args()
+    need = lib.diffattn_decode_workspace_bytes(ctypes.byref(a))
+    assert lib.diffattn_decode(ctypes.byref(a), FAKE + 6 * (1 << 34), need - 1, None) == da.EWORKSPACE
+    assert lib.diffattn_decode(ctypes.byref(a), None, need, None) == da.EWORKSPACE
+
+
+def test_lambda_rejects(lib):
+    f = lib.diffattn_lambda
+    assert f(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, 0, 8, 1, FAKE + 65536, None) == da.EINVAL
+    assert f(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, 4, 8, 0, FAKE + 65536, None) == da.EINVAL
+    assert f(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, 4, 8, 1, FAKE + 8, None) == da.EINVAL  # alias

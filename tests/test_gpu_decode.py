@@ -1,0 +1,161 @@
+"""GPU parity of the split-KV paged decode against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import check, dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+@pytest.fixture(scope="module")
+def da():
+    import differential_attention_amd as m
+    m.load_library()
+    return m
+
+
+class DecodeCase:
+    def __init__(self, d: W.Decode, torch, da):
+        self.d, self.torch, self.da = d, torch, da
+        qf = to_dev(d.q_full, "bf16")
+        self.q1, self.q2 = qf[:, 0::2], qf[:, 1::2]
+        self.kc = to_dev(d.k1_cache, "bf16")
+        self.vc = to_dev(d.v_cache, "bf16")
+        self.table = torch.from_numpy(d.page_table).to(dev())
+        self.ctx = torch.from_numpy(d.ctx_len).to(dev())
+        self.lam64 = oracle.lambda_(d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2, d.depth)
+        vecs = [torch.from_numpy(x).to(dev()) for x in (d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2)]
+        self.lam = da.lambda_(*vecs, d.depth)
+        self.gamma = None
+
+    def run(self, **kw):
+        d = self.d
+        args = dict(depth=d.depth, norm=d.norm, gamma=self.gamma, eps=d.eps)
+        args.update(kw)
+        return self.da.decode(self.q1, self.q2, self.kc, self.vc, self.table, self.ctx, self.lam, **args)
+
+    def oracle(self, seqs=None, norm=None, gamma=None):
+        """Oracle on all sequences, or on a subset with their pages compacted."""
+        d = self.d
+        norm = d.norm if norm is None else norm
+        if seqs is None:
+            kc = d.f32("k1_cache")
+            return oracle.decode(d.f32("q1"), d.f32("q2"), kc, kc, d.f32("v_cache"), d.page_table,
+                                 d.ctx_len, self.lam64, depth=d.depth, norm=norm, gamma=gamma)
+        seqs = np.asarray(seqs)
+        npg = (d.ctx_len[seqs] + d.page - 1) // d.page
+        used = np.concatenate([d.page_table[b, :n] for b, n in zip(seqs, npg)])
+        remap = {int(p): i for i, p in enumerate(used)}
+        table = np.full((len(seqs), d.max_pages), -1, np.int32)
+        for r, (b, n) in enumerate(zip(seqs, npg)):
+            table[r, :n] = [remap[int(p)] for p in d.page_table[b, :n]]
+        kc = W.bf16_to_f32(d.k1_cache[used])
+        vc = W.bf16_to_f32(d.v_cache[used])
+        return oracle.decode(d.f32("q1")[seqs], d.f32("q2")[seqs], kc, kc, vc, table, d.ctx_len[seqs],
+                             self.lam64, depth=d.depth, norm=norm, gamma=gamma)
+
+
+def small(B=6, lens=None, H=8, H_kv=2, seed=0, max_pages=16):
+    if lens is None:
+        return W.decode_v2(seed=seed, B=B, H=H, H_kv=H_kv, max_pages=max_pages, ctx_lo=1, ctx_hi=max_pages * 64)
+    return W.decode_v2(seed=seed, B=len(lens), H=H, H_kv=H_kv, max_pages=max_pages, ctx_len=np.array(lens))
+
+
+@pytest.mark.parametrize("lens", [[1, 63, 64, 65, 128, 1000], [1024, 777, 5, 129]])
+@pytest.mark.parametrize("split_pages", [0, 1, 3])
+def test_decode_ragged(torch, da, lens, split_pages):
+    c = DecodeCase(small(lens=lens), torch, da)
+    say(f"decode lens {lens} split_pages {split_pages}")
+    check(c.run(split_pages=split_pages).float().cpu().numpy(), c.oracle(), "bf16", "decode")
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 8), (16, 2), (4, 4), (6, 2)])
+def test_decode_groupings(torch, da, H, H_kv):
+    c = DecodeCase(small(B=5, H=H, H_kv=H_kv, seed=H), torch, da)
+    say(f"decode H {H} H_kv {H_kv}")
+    check(c.run().float().cpu().numpy(), c.oracle(), "bf16", "decode grouping")
+
+
+def test_decode_rms_norm(torch, da):
+    c = DecodeCase(small(B=4, seed=5), torch, da)
+    gamma = np.random.default_rng(5).uniform(0.9, 1.1, (c.d.H, 128)).astype(np.float32)
+    got = c.run(norm=True, gamma=torch.from_numpy(gamma).to(dev())).float().cpu().numpy()
+    check(got, c.oracle(norm=True, gamma=gamma), "bf16", "decode RMS norm")
+
+
+def test_decode_page_permutation_is_bitwise_invariant(torch, da):
+    d = small(B=4, seed=6)
+    c = DecodeCase(d, torch, da)
+    a = c.run().clone()
+    perm = np.random.default_rng(1).permutation(d.num_pages)
+    inv = np.argsort(perm)  # new physical page of old page p is inv[p]
+    kc = np.empty_like(d.k1_cache)
+    vc = np.empty_like(d.v_cache)
+    kc[inv] = d.k1_cache
+    vc[inv] = d.v_cache
+    table = np.where(d.page_table >= 0, inv[np.maximum(d.page_table, 0)], -1).astype(np.int32)
+    c.kc, c.vc = to_dev(kc, "bf16"), to_dev(vc, "bf16")
+    c.table = torch.from_numpy(table).to(dev())
+    assert torch.equal(a, c.run())
+
+
+def test_decode_matches_prefill_last_row(torch, da):
+    # one sequence of length L stored in pages in order equals the last row of
+    # a causal V2 prefill over the same tokens
+    L, H, H_kv = 300, 8, 2
+    d = small(lens=[L], H=H, H_kv=H_kv, seed=8)
+    c = DecodeCase(d, torch, da)
+    dec = c.run().float()
+    npg = (L + 63) // 64
+    pages = d.page_table[0, :npg]
+    k = d.k1_cache[pages].transpose(1, 0, 2, 3).reshape(H_kv, npg * 64, 128)[:, :L][None]
+    v = d.v_cache[pages].transpose(1, 0, 2, 3).reshape(H_kv, npg * 64, 128)[:, :L][None]
+    q = np.zeros((1, 2 * H, L, 128), np.uint16)
+    q[0, :, L - 1] = d.q_full[0]
+    qd = to_dev(q, "bf16")
+    kd = to_dev(k, "bf16")
+    pre = da.prefill(qd[:, 0::2], qd[:, 1::2], kd, kd, to_dev(v, "bf16"), c.lam, depth=d.depth,
+                     causal=True)
+    diff = (pre[0, :, L - 1].float() - dec[0]).abs().max().item()
+    assert diff <= 1.6e-2, diff
+
+
+def test_decode_reports_bad_page_and_length(torch, da):
+    d = small(lens=[200, 130, 64], seed=9)
+    table0 = d.page_table.copy()
+    d.page_table[1, 2] = d.num_pages + 5   # out of range: its tokens (128, 129) are masked, bit 0
+    d.ctx_len[2] = 0                        # invalid length: bit 1, zero output
+    c = DecodeCase(d, torch, da)
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    out = c.run(dev_err=err).float().cpu().numpy()
+    assert err.item() == 3
+    kc, vc = d.f32("k1_cache"), d.f32("v_cache")
+    q1, q2 = d.f32("q1"), d.f32("q2")
+    ref0 = oracle.decode(q1[:1], q2[:1], kc, kc, vc, table0[:1], np.array([200], np.int32), c.lam64,
+                         depth=d.depth, norm=False)
+    check(out[:1], ref0, "bf16", "decode seq 0 beside bad entries")
+    # sequence 1 equals attention over its first two pages (the bad page is masked)
+    table1 = table0[1:2].copy()
+    table1[0, 2:] = -1
+    ref1 = oracle.decode(q1[1:2], q2[1:2], kc, kc, vc, table1, np.array([128], np.int32), c.lam64,
+                         depth=d.depth, norm=False)
+    check(out[1:2], ref1, "bf16", "decode seq 1 with its bad page masked")
+    assert np.all(out[2] == 0)
+
+
+def test_decode_v2_full(torch, da):
+    d = W.decode_v2()
+    say(f"decode_v2 full: 64 sequences, {d.num_pages} pages, context {d.ctx_len.min()}..{d.ctx_len.max()}")
+    c = DecodeCase(d, torch, da)
+    out = c.run().float().cpu().numpy()
+    seqs = np.array([0, 7, int(np.argmax(d.ctx_len)), int(np.argmin(d.ctx_len)), 33, 63])
+    check(out[seqs], c.oracle(seqs=seqs), "bf16", "decode_v2 sampled sequences")

@@ -1,0 +1,183 @@
+"""GPU parity of lambda and prefill against the fp64 oracle, through the C ABI.
+
+Tolerances: bf16 inputs with fp32 accumulation: max |error| <= 2e-2 and
+relative Frobenius error <= 1e-2; the fp32 path: max |error| <= 1e-5."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import (PrefillCase, check, dev, gather_rows, sampled_rows, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+@pytest.fixture(scope="module")
+def da():
+    import differential_attention_amd as m
+    m.load_library()
+    return m
+
+
+# ---------------------------------------------------------------- lambda
+
+@pytest.mark.parametrize("H,dl,depth", [(1, 64, 1), (16, 64, 12), (32, 128, 20), (8, 64, 12), (5, 1000, 3)])
+def test_lambda_parity(torch, da, H, dl, depth):
+    rng = np.random.default_rng(H * 1000 + dl)
+    vecs = [(rng.standard_normal((H, dl)) * 0.1).astype(np.float32) for _ in range(4)]
+    got = da.lambda_(*(torch.from_numpy(v).to(dev()) for v in vecs), depth).cpu().numpy()
+    ref = oracle.lambda_(*vecs, depth)
+    # fp32 evaluation of exp(a) - exp(b) + init: the terms are O(1), so a few
+    # fp32 ulps of 1 bound the error (relative error is meaningless when they cancel)
+    assert np.max(np.abs(got - ref)) <= 1e-6
+
+
+# ---------------------------------------------------------------- fp32 path
+
+def test_tiny_v1_fp32(torch, da):
+    c = PrefillCase(W.tiny_v1())
+    say("tiny_v1 fp32 (1 head, N 128, causal, RMS)")
+    got = c.run().cpu().numpy()
+    check(got, c.oracle(), "f32", "tiny_v1")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("N,dqk,dv,H,Hkv,norm", [(1, 64, 128, 1, 1, True), (77, 48, 80, 4, 2, False),
+                                                  (130, 128, 128, 2, 1, True), (65, 3, 5, 2, 2, False)])
+def test_fp32_variants(torch, da, causal, N, dqk, dv, H, Hkv, norm):
+    rng = np.random.default_rng(N + dqk)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    p = W.Prefill("f32case", "f32", 2, H, Hkv, N, dqk, dv, f(2, H, N, dqk), f(2, H, N, dqk),
+                  f(2, Hkv, N, dqk), f(2, Hkv, N, dqk), f(2, Hkv, N, dv),
+                  *(0.1 * f(H, dqk) for _ in range(4)), depth=4, causal=causal, norm=norm,
+                  gamma=rng.uniform(0.9, 1.1, (H, dv)).astype(np.float32) if norm else None)
+    c = PrefillCase(p)
+    say(f"f32 N {N} dqk {dqk} dv {dv} H {H}/{Hkv} causal {causal} norm {norm}")
+    check(c.run().cpu().numpy(), c.oracle(), "f32", "f32 variant")
+
+
+# ---------------------------------------------------------------- bf16 path, small shapes
+
+def _bf16_case(form, N, causal, B=2, seed=0, shared=None, norm=None):
+    if form == "v1":
+        p = W.prefill_v1(seed=seed, B=B, H=3, N=N, causal=causal)
+    else:
+        p = W.prefill_v2(seed=seed, B=B, H=4, H_kv=2, N=N, causal=causal)
+    if shared is not None and shared != p.shared_k:
+        if shared:
+            p.k2 = p.k1
+        else:
+            rng = np.random.default_rng(seed + 99)
+            p.k2 = W.f32_to_bf16(rng.standard_normal(p.k1.shape).astype(np.float32))
+        p.shared_k = shared
+    if norm is not None and norm != p.norm:
+        p.norm = norm
+        p.gamma = np.random.default_rng(seed).uniform(0.9, 1.1, (p.H, p.d_v)).astype(np.float32) if norm else None
+    return p
+
+
+@pytest.mark.parametrize("form", ["v1", "v2"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("N", [1, 31, 64, 200, 333])
+def test_bf16_small(torch, da, form, causal, N):
+    p = _bf16_case(form, N, causal, seed=N)
+    c = PrefillCase(p)
+    say(f"bf16 {form} N {N} causal {causal}")
+    check(c.run().float().cpu().numpy(), c.oracle(), "bf16", f"{form} N={N}")
+
+
+@pytest.mark.parametrize("form,shared,norm", [("v1", True, True), ("v1", False, False), ("v1", True, False),
+                                              ("v2", False, False), ("v2", True, True), ("v2", False, True)])
+def test_bf16_all_kernel_variants(torch, da, form, shared, norm):
+    p = _bf16_case(form, 257, True, B=1, seed=7, shared=shared, norm=norm)
+    c = PrefillCase(p)
+    say(f"bf16 variant {form} shared_k {shared} norm {norm}")
+    check(c.run().float().cpu().numpy(), c.oracle(), "bf16", f"{form}/{shared}/{norm}")
+
+
+def test_bf16_explicit_scale_and_strided_out(torch, da):
+    p = _bf16_case("v2", 150, True, B=1, seed=3)
+    c = PrefillCase(p)
+    big = torch.zeros((1, p.N, p.H, 128), dtype=torch.bfloat16, device=dev())
+    out = big.permute(0, 2, 1, 3)  # [B, H, N, d] view with the head stride 128
+    c.run(scale=0.05, out=out)
+    ref = oracle.prefill(p.f32("q1"), p.f32("q2"), p.f32("k1"), p.f32("k1"), p.f32("v"), c.lam64,
+                         depth=p.depth, causal=True, norm=False, scale=0.05)
+    check(out.float().cpu().numpy(), ref, "bf16", "scale 0.05, [B,N,H,d] output")
+
+
+# ---------------------------------------------------------------- invariants (bitwise)
+
+def test_lambda_zero_ignores_branch_two(torch, da):
+    c = PrefillCase(_bf16_case("v1", 190, True, B=1, seed=11))
+    zero = torch.zeros(c.p.H, dtype=torch.float32, device=dev())
+    a = c.run(lam=zero).clone()
+    c.q2 = torch.randn_like(c.q2.float()).to(torch.bfloat16)
+    c.k2 = torch.randn_like(c.k2.float()).to(torch.bfloat16)
+    b = c.run(lam=zero)
+    assert torch.equal(a, b)
+
+
+def test_identical_branches_lambda_one_is_zero(torch, da):
+    for form in ("v1", "v2"):
+        c = PrefillCase(_bf16_case(form, 130, True, B=1, seed=12))
+        c.q2, c.k2 = c.q1, c.k1
+        one = torch.ones(c.p.H, dtype=torch.float32, device=dev())
+        out = c.run(lam=one)
+        assert torch.count_nonzero(out).item() == 0
+
+
+def test_causality_and_determinism(torch, da):
+    c = PrefillCase(_bf16_case("v2", 300, True, B=1, seed=13))
+    a = c.run().clone()
+    assert torch.equal(a, c.run())  # run to run
+    r = 150
+    k1 = c.k1.clone()
+    v = c.v.clone()
+    k1[:, :, r + 1:] = torch.randn_like(k1[:, :, r + 1:].float()).to(torch.bfloat16)
+    v[:, :, r + 1:] = torch.randn_like(v[:, :, r + 1:].float()).to(torch.bfloat16)
+    c.k1 = c.k2 = k1
+    c.v = v
+    b = c.run()
+    assert torch.equal(a[:, :, :r + 1], b[:, :, :r + 1])
+    assert not torch.equal(a[:, :, r + 1:], b[:, :, r + 1:])
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def test_prefill_v1_full(torch, da):
+    p = W.prefill_v1()
+    c = PrefillCase(p)
+    say("prefill_v1 full: B 2, H 16, N 4096, d_qk 64, d_v 128, causal, RMS")
+    out = c.run()
+    torch.cuda.synchronize()
+    rows = sampled_rows(p.B, p.H, p.N, seed=21)
+    check(gather_rows(out, rows, p.H, p.N), c.oracle(rows=rows), "bf16", "prefill_v1 sampled rows")
+
+
+def test_prefill_v2_full(torch, da):
+    p = W.prefill_v2()
+    c = PrefillCase(p)
+    say("prefill_v2 full: 64 query heads / 8 KV heads, N 16384, d 128, causal")
+    out = c.run()
+    torch.cuda.synchronize()
+    rows = sampled_rows(p.B, p.H, p.N, seed=22, n_rand=48, edge=16)
+    check(gather_rows(out, rows, p.H, p.N), c.oracle(rows=rows), "bf16", "prefill_v2 sampled rows")
+
+
+def test_longctx_v1_full(torch, da):
+    p = W.longctx_v1()
+    c = PrefillCase(p)
+    say("longctx_v1 full: H 8, N 65536, planted keys, causal, RMS")
+    out = c.run()
+    torch.cuda.synchronize()
+    probe_rows = lambda b, h: np.unique(np.concatenate([p.probes[b, h, :, 0], p.probes[b, h, :, 1]]))
+    rows = sampled_rows(p.B, p.H, p.N, seed=23, n_rand=16, edge=8, extra=probe_rows)
+    check(gather_rows(out, rows, p.H, p.N), c.oracle(rows=rows), "bf16", "longctx_v1 sampled + probe rows")
