@@ -62,7 +62,7 @@ int diffattn_prefill(const diffattn_prefill_args *a, void *stream) {
 size_t diffattn_decode_workspace_bytes(const diffattn_decode_args *a) {
     da::DecodePlan plan;
     std::string msg;
-    if (da::check_decode(a, &plan, &msg) != DIFFATTN_OK) return 0;
+    if (da::check_decode_sizes(a, &plan, &msg) != DIFFATTN_OK) return 0;
     return plan.ws_bytes;
 }
 

@@ -59,8 +59,17 @@ __device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uin
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Value of the lane l ^ 32 (the other half of the wave).
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine a value with the one held by lane l ^ 32 (the other half of the
+// wave) using v_permlane32_swap (a VALU lane swap, no LDS round trip): with
+// both operands = x, the two results hold x[l % 32] and x[32 + l % 32].
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float wave_max(float x) {
     for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));

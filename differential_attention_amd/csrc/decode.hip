@@ -249,7 +249,11 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
         }
         ob[br] = lsum > 0.0f ? acc / lsum : 0.0f;
     }
-    float y = ob[0] - p.lambda[h] * ob[1];
+    float y;
+    {
+#pragma clang fp contract(off)
+        y = ob[0] - p.lambda[h] * ob[1];
+    }
     if (p.norm) {
         float ss = wave_sum(y * y);
         if ((dv & 63) == 0) red[dv >> 6] = ss;

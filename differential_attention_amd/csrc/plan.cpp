@@ -168,7 +168,7 @@ int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string
     return DIFFATTN_OK;
 }
 
-int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *msg) {
+int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::string *msg) {
     *plan = DecodePlan();
     if (!a) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: null argument struct");
     if (a->dtype != DIFFATTN_BF16 && a->dtype != DIFFATTN_F32)
@@ -213,7 +213,12 @@ int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *m
     plan->ws_bytes = (size_t)(a->B > 0 ? a->B : 0) * a->H_kv * plan->num_splits * plan->qrows *
                      (size_t)(a->d_v + 2) * sizeof(float);
 
-    if (a->B == 0) return DIFFATTN_OK;
+    return DIFFATTN_OK;
+}
+
+int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *msg) {
+    int rc = check_decode_sizes(a, plan, msg);
+    if (rc != DIFFATTN_OK || a->B == 0) return rc;
     if (!a->q1 || !a->q2 || !a->k1_cache || !a->v_cache || !a->page_table || !a->ctx_len ||
         !a->lambda || !a->out)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: null pointer");

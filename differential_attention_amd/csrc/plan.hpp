@@ -37,6 +37,10 @@ double lambda_init(int depth);
 // Validate prefill arguments. Returns DIFFATTN_OK or a negative status with *msg set.
 int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string *msg);
 
+// Validate the sizes and flags of decode arguments (no pointer is examined)
+// and build the plan.
+int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::string *msg);
+
 // Validate decode arguments (workspace excluded) and build the plan.
 int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *msg);
 

@@ -95,8 +95,12 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillF32Params p) {
 
     const float lam = p.lambda[h];
     const float r1 = 1.0f / l1, r2 = lam / l2;
-    float ya = c0 < p.d_v ? o1a * r1 - o2a * r2 : 0.0f;
-    float yb = c1 < p.d_v ? o1b * r1 - o2b * r2 : 0.0f;
+    float ya, yb;
+    {
+#pragma clang fp contract(off)
+        ya = c0 < p.d_v ? o1a * r1 - o2a * r2 : 0.0f;
+        yb = c1 < p.d_v ? o1b * r1 - o2b * r2 : 0.0f;
+    }
     if (p.norm) {
         const float ss = wave_sum(ya * ya + yb * yb);
         const float rs = p.one_minus_init / sqrtf(ss / (float)p.d_v + p.eps);

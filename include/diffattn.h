@@ -143,7 +143,8 @@ int diffattn_prefill(const diffattn_prefill_args *a, void *stream);
 
 /*
  * Bytes of device workspace diffattn_decode needs for these arguments
- * (split-KV partial results). Returns 0 if the arguments are invalid.
+ * (split-KV partial results). Only sizes and flags are examined (pointers
+ * may be NULL). Returns 0 if they are invalid.
  */
 size_t diffattn_decode_workspace_bytes(const diffattn_decode_args *a);
 

@@ -177,7 +177,7 @@ def test_decode_workspace_and_plan(lib):
     ("d_qk", 64, da.EUNSUPPORTED),
     ("page_size", 32, da.EUNSUPPORTED),
     ("dtype", da.F32, da.EUNSUPPORTED),
-    ("H", 40, da.EINVAL),               # not a multiple of H_kv
+    ("H", 36, da.EINVAL),               # not a multiple of H_kv
     ("k2_cache", FAKE + 5 * (1 << 34), da.EUNSUPPORTED),
     ("page_table", None, da.EINVAL),
     ("split_pages", -1, da.EINVAL),
@@ -200,3 +200,11 @@ def test_lambda_rejects(lib):
     assert f(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, 0, 8, 1, FAKE + 65536, None) == da.EINVAL
     assert f(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, 4, 8, 0, FAKE + 65536, None) == da.EINVAL
     assert f(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, 4, 8, 1, FAKE + 8, None) == da.EINVAL  # alias
+
+
+def test_decode_workspace_needs_no_pointers(lib):
+    a = _decode_args(q1=None, q2=None, k1_cache=None, k2_cache=None, v_cache=None, page_table=None,
+                     ctx_len=None, lambda_=None, out=None)
+    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) > 0
+    a = _decode_args(H=36)   # invalid sizes still give 0
+    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == 0
