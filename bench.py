@@ -106,6 +106,79 @@ def cpu_baseline(p, lam64, budget_s):
                       f"{t:.1f} s, FLOPs counted per visible key as for the GPU"}
 
 
+def single_workload(args, torch, da, W, dev):
+    """Time one workload alone: one call per step, HIP events around each call."""
+    stream = torch.cuda.current_stream()
+
+    def to_dev(x, dtype="bf16"):
+        x = np.ascontiguousarray(x)
+        if dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    name = args.workload
+    if name == "copy":
+        n = 1 << 31  # 2 Gi bf16 elements = 4 GiB read + 4 GiB written
+        src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        call = lambda: dst.copy_(src)
+        work, unit, metric, bound = 2.0 * n * 2, "GB/s", "device copy GB/s (read + write)", "hbm"
+        desc = "torch copy_ of 2^31 bf16 elements (4 GiB read, 4 GiB written)"
+    elif name == "decode_v2":
+        d = W.decode_v2()
+        qd = to_dev(d.q_full)
+        kc, vc = to_dev(d.k1_cache), to_dev(d.v_cache)
+        table, ctx = torch.from_numpy(d.page_table).to(dev), torch.from_numpy(d.ctx_len).to(dev)
+        lam = da.lambda_(*(torch.from_numpy(x).to(dev) for x in (d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2)), d.depth)
+        out = torch.empty((d.B, d.H, d.d_v), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(da.decode_workspace_bytes(qd[:, 0::2], qd[:, 1::2], kc, vc, table, ctx, lam,
+                                                   depth=d.depth), dtype=torch.uint8, device=dev)
+        call = lambda: da.decode(qd[:, 0::2], qd[:, 1::2], kc, vc, table, ctx, lam, depth=d.depth, out=out,
+                                 workspace=ws)
+        work, unit, metric, bound = decode_bytes(d), "GB/s", "decode GB/s (algorithmic HBM bytes)", "hbm"
+        desc = "decode_v2: V2 paged decode, 64 seqs, ctx U{8192..32768}, 8 KV / 64 Q heads, d 128, page 64"
+    else:
+        p = getattr(W, name)()
+        dt = p.dtype
+        if p.q_full is not None:
+            qf = to_dev(p.q_full, dt)
+            q1, q2 = qf[:, 0::2], qf[:, 1::2]
+        else:
+            q1, q2 = to_dev(p.q1, dt), to_dev(p.q2, dt)
+        k1 = to_dev(p.k1, dt)
+        k2 = k1 if p.shared_k else to_dev(p.k2, dt)
+        v = to_dev(p.v, dt)
+        gamma = torch.from_numpy(p.gamma).to(dev) if p.norm else None
+        lam = da.lambda_(*(torch.from_numpy(x).to(dev) for x in (p.lam_q1, p.lam_k1, p.lam_q2, p.lam_k2)), p.depth)
+        out = torch.empty((p.B, p.H, p.N, p.d_v), dtype=q1.dtype, device=dev)
+        call = lambda: da.prefill(q1, q2, k1, k2, v, lam, depth=p.depth, causal=p.causal, norm=p.norm,
+                                  gamma=gamma, eps=p.eps, out=out)
+        work = prefill_flops(p.B, p.H, p.N, p.d_qk, p.d_v)
+        unit, metric, bound = "TFLOP/s", "prefill TFLOP/s", "mfma"
+        desc = f"{name}: B {p.B}, H {p.H}, H_kv {p.H_kv}, N {p.N}, d_qk {p.d_qk}, d_v {p.d_v}, {p.dtype}"
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    val = work / (ms * 1e-3) / scale
+    peak = BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBS
+    dtype = "f32" if name == "tiny_v1" else "bf16"
+    line = {"metric": metric, "value": val, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": {"workload": desc},
+            "roofline": {"bound": bound, "achieved": val, "peak": peak, "unit": unit, "frac": val / peak,
+                         "traffic": load_traffic(name)}}
+    log(f"{name}: {ms * 1e3:.1f} us per call, {val:.1f} {unit} ({100 * val / peak:.1f}% of peak)")
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +188,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profiling aid: run only one part of the step")
+    ap.add_argument("--workload", default="step",
+                    choices=["step", "prefill_v1", "prefill_v2", "longctx_v1", "tiny_v1", "decode_v2", "copy"],
+                    help="step: the whole path (default); otherwise time one workload alone "
+                         "(copy: a plain device copy of 4 GiB, for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -134,6 +211,10 @@ def main():
 
     def to_dev(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.workload != "step":
+        single_workload(args, torch, da, W, dev)
+        return
 
     t_gen = time.perf_counter()
     p = W.prefill_v1()

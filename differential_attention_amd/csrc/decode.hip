@@ -4,16 +4,21 @@
 // every key/value byte feeds all query heads of its group, both branches).
 //
 // Pass 1 (decode_split_kernel), one work-group per (split s, KV head g,
-// sequence b): the pages of the split stream HBM -> registers -> LDS (the
-// next page's loads are in flight while the current page is used). All
-// 2 * group query rows of the KV head (both branches of every pair) are one
-// 16-column MFMA operand, so each K and V page is read from HBM exactly once.
-// Each of the 4 waves takes 16 tokens of a page:
-//   S^T = K Q^T         16 tokens x 16 query rows, v_mfma_f32_16x16x32_bf16
-//   online softmax      per query row (lane % 16), running max / sum
-//   O^T += V^T P^T      128 x 16, v_mfma_f32_16x16x16_bf16; the 4 scores a
-//                       lane holds are exactly its B-operand k-slots, and V
-//                       is transposed into LDS so V^T is read 8 bytes at a time
+// sequence b). All 2 * group query rows of the KV head (both branches of
+// every pair) form one 16-column MFMA operand, so each K and V byte is read
+// from HBM exactly once. Each of the 4 waves owns a 16-token slice of every
+// page of the split and streams it independently -- no barrier inside the
+// page loop: the next kBuf pages' K and V slices are loaded into registers
+// while the current one is used, so every wave keeps HBM requests in flight.
+//   S^T = K Q^T      16 tokens x 16 query rows, v_mfma_f32_16x16x32_bf16;
+//                    each lane loads its K operand (token, 8 features)
+//                    straight from HBM in MFMA operand layout
+//   online softmax   per query row (lane % 16), running max / sum
+//   O^T += V^T P^T   128 x 16, v_mfma_f32_16x16x16_bf16: the 4 scores a lane
+//                    holds are its B-operand k-slots; the V slice goes through
+//                    a wave-private LDS buffer (XOR-swizzled rows) and
+//                    ds_read_b64_tr_b16 returns 4 consecutive tokens of one
+//                    value column
 // At the end the 4 waves' states are merged through LDS and the split's
 // (max, sum, unnormalised O) per query row is written to the workspace.
 // Pass 2 (decode_combine_kernel), one work-group per (output head, sequence):
@@ -21,8 +26,10 @@
 // y = O1 - lambda O2 and, for the V1 norm, y / sqrt(mean(y^2) + eps) *
 // gamma * (1 - lambda_init).
 // Token t of sequence b is slot t % 64 of page page_table[b][t / 64]; tokens
-// at or past ctx_len[b] are masked. A page id outside [0, num_pages) is
-// never dereferenced: its tokens are masked and bit 0 of *dev_err is set.
+// at or past ctx_len[b] are masked and their value rows replaced by zeros, so
+// whatever an unused cache slot holds cannot reach the output. A page id
+// outside [0, num_pages) is never dereferenced: page 0 is read in its place,
+// all its tokens are masked and bit 0 of *dev_err is set.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -31,13 +38,15 @@ namespace da {
 namespace {
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kD = 128;      // d_qk = d_v
 constexpr int kPage = 64;    // tokens per page
-constexpr int kKLd = kD + 8;         // K tile row stride (elements)
-constexpr int kVtLd = kPage + 8;     // V^T tile row stride (elements)
-constexpr int kKElems = kPage * kKLd;
-constexpr int kVtElems = kD * kVtLd;
+#ifndef DIFFATTN_DECODE_KBUF
+#define DIFFATTN_DECODE_KBUF 2
+#endif
+constexpr int kBuf = DIFFATTN_DECODE_KBUF;  // pages of K/V held in registers per wave
 
 struct DecodeParams {
     const __bf16 *q1, *q2;
@@ -55,8 +64,15 @@ struct DecodeParams {
 
 __device__ __forceinline__ uint4 ldg16(const __bf16 *p) { return *(const uint4 *)p; }
 
+// one wave's 16-token slice of a page: K operands and V rows
+struct Slice {
+    uint4 k[4];  // k[kc]: token 16 w + lane % 16, features 32 kc + 8 (lane / 16) .. +7
+    uint4 v[4];  // v[i]: token 16 w + 4 i + lane / 16, features 8 (lane % 16) .. +7
+    bool ok;     // the page id was valid
+};
+
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
-    __shared__ __attribute__((aligned(16))) __bf16 lds[kKElems + kVtElems];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * 16 * kD * 4];  // 32 KB
     __shared__ float red_m[4][16], red_l[4][16];
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -72,6 +88,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int pb = s * p.split_pages;
     const int pe = min(npages, pb + p.split_pages);
     if (pb >= pe) return;
+    const int np = pe - pb;
 
     // Q^T fragments: lane supplies query row n, d = 32 kc + 8 grp .. +7
     bf16x8 qf[4];
@@ -87,76 +104,59 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         }
     }
 
+    // the split's page ids (at most 64), one per lane, read once; each page's id
+    // is then taken with v_readlane (a scalar), so no vector load of the table
+    // sits between the K/V loads of consecutive pages
     const int32_t *table = p.page_table + (int64_t)b * p.max_pages;
-    uint4 kr[4], vr[4];
-    bool page_ok = true;
-    auto load_page = [&](int pg) {
-        const int phys = table[pg];
-        page_ok = phys >= 0 && phys < p.num_pages;
-        const int64_t base = page_ok ? ((int64_t)phys * p.H_kv + g) * kPage : 0;
-        const __bf16 *kp = p.kc + base * kD;
-        const __bf16 *vp = p.vc + base * kD;
-        uint4 z = {0u, 0u, 0u, 0u};
+    const int ids = lane < np ? table[pb + lane] : 0;
+    bool bad_page = false;
+    auto load = [&](Slice &S, int k) {
+        int phys = __builtin_amdgcn_readlane(ids, k);
+        S.ok = phys >= 0 && phys < p.num_pages;
+        bad_page |= !S.ok;
+        phys = S.ok ? phys : 0;
+        const int64_t base = (((int64_t)phys * p.H_kv + g) * kPage + 16 * wave) * kD;
+        const __bf16 *kp = p.kc + base + n * kD + 8 * grp;
+        const __bf16 *vp = p.vc + base + grp * kD + 8 * n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
-            kr[i] = page_ok ? ldg16(kp + (c >> 4) * kD + (c & 15) * 8) : z;
-        }
+        for (int kc = 0; kc < 4; ++kc) S.k[kc] = ldg16(kp + 32 * kc);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int task = tid + 256 * i;
-            const int j = task & 31, cg = task >> 5;
-            vr[2 * i] = page_ok ? ldg16(vp + (2 * j) * kD + 8 * cg) : z;
-            vr[2 * i + 1] = page_ok ? ldg16(vp + (2 * j + 1) * kD + 8 * cg) : z;
-        }
-    };
-    auto store_page = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
-            *(uint4 *)(lds + (c >> 4) * kKLd + (c & 15) * 8) = kr[i];
-        }
-        uint32_t *vt = (uint32_t *)(lds + kKElems);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int task = tid + 256 * i;
-            const int j = task & 31, cg = task >> 5;
-            const uint4 a = vr[2 * i], c = vr[2 * i + 1];
-            const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-            const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (e & 1) ? (aw[e >> 1] >> 16) : (aw[e >> 1] & 0xffffu);
-                const uint32_t hi = (e & 1) ? (cw[e >> 1] & 0xffff0000u) : (cw[e >> 1] << 16);
-                vt[(8 * cg + e) * (kVtLd / 2) + j] = lo | hi;
-            }
-        }
+        for (int i = 0; i < 4; ++i) S.v[i] = ldg16(vp + 4 * i * kD);
     };
 
     f32x4 o[8];
 #pragma unroll
     for (int dc = 0; dc < 8; ++dc) o[dc] = f32x4{};
     float m = -INFINITY, l = 0.0f;
-    bool bad_page = false;
 
-    load_page(pb);
-    for (int pg = pb; pg < pe; ++pg) {
-        const bool cur_ok = page_ok;
-        bad_page |= !cur_ok;
-        __syncthreads();
-        store_page();
-        __syncthreads();
-        if (pg + 1 < pe) load_page(pg + 1);
+    // this wave's V buffer: 16 rows x 256 bytes, 16-byte chunks XOR-swizzled
+    // by 2 (row & 7) so each transposing read pass touches 64 distinct banks
+    unsigned char *vbuf = lds + wave * 4096;
+    const int vrow = 4 * grp + (n >> 2);  // row this lane addresses in a transposing read
+    const int vswz = (vrow & 7) << 1;
 
-        // scores of this wave's 16 tokens against the 16 query rows
-        f32x4 sc = f32x4{};
-        const __bf16 *krp = lds + (16 * wave + n) * kKLd + 8 * grp;
+    auto process = [&](const Slice &S, int k) {
+        const int pg = pb + k;
+        const int vis = L - pg * kPage - 16 * wave;  // visible rows of this slice
+        // V rows into the wave buffer (rows past the end as zeros)
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) sc = mfma16(as_bf16x8(*(const uint4 *)(krp + 32 * kc)), qf[kc], sc);
-        const int tok0 = pg * kPage + 16 * wave + 4 * grp;
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * i + grp;
+            const uint32_t keep = row < vis ? 0xffffffffu : 0u;  // select by value, not by address
+            uint4 v = S.v[i];
+            v.x &= keep;
+            v.y &= keep;
+            v.z &= keep;
+            v.w &= keep;
+            *(uint4 *)(vbuf + row * 256 + 16 * (n ^ ((row & 7) << 1))) = v;
+        }
+        // scores of the 16 tokens against the 16 query rows
+        f32x4 sc = f32x4{};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) sc = mfma16(as_bf16x8(S.k[kc]), qf[kc], sc);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            if (!cur_ok || tok0 + r >= L) sc[r] = -INFINITY;
+            if (!S.ok || 4 * grp + r >= vis) sc[r] = -INFINITY;
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -168,26 +168,45 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(fmaf(sc[r], p.sc_log2, -msub));
         l = l * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        if (alpha != 1.0f) {
 #pragma unroll
-            for (int dc = 0; dc < 8; ++dc) o[dc] *= alpha;
-        }
+        for (int dc = 0; dc < 8; ++dc) o[dc] *= alpha;
         const bf16x2 p01 = pack2(pr[0], pr[1]), p23 = pack2(pr[2], pr[3]);
         const bf16x4_t pb4 = {p01[0], p01[1], p23[0], p23[1]};
-        const __bf16 *vrp = lds + kKElems + n * kVtLd + 16 * wave + 4 * grp;
+        // the V rows written above must be complete before other lanes read them
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        const unsigned char *vr = vbuf + vrow * 256;
 #pragma unroll
         for (int dc = 0; dc < 8; ++dc) {
-            const bf16x4_t va = *(const bf16x4_t *)(vrp + 16 * dc * kVtLd);
-            o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb4, o[dc], 0, 0, 0);
+            const int col = 16 * dc + 4 * (n & 3);
+            const int c = (col >> 3) ^ vswz;
+            const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 16 * c + 2 * (col & 7)));
+            o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, va), pb4, o[dc], 0, 0, 0);
+        }
+        // the reads must be complete before the next slice overwrites the buffer
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+    };
+
+    Slice S[kBuf];
+#pragma unroll
+    for (int j = 0; j < kBuf; ++j)
+        if (j < np) load(S[j], j);
+    for (int k0 = 0; k0 < np; k0 += kBuf) {
+#pragma unroll
+        for (int j = 0; j < kBuf; ++j) {
+            const int k = k0 + j;
+            if (k < np) {
+                process(S[j], k);
+                if (k + kBuf < np) load(S[j], k + kBuf);
+            }
         }
     }
-    if (bad_page && tid == 0 && p.dev_err) atomicOr(p.dev_err, 1);
+    if (bad_page && lane == 0 && p.dev_err) atomicOr(p.dev_err, 1);
 
     // row sums over the 4 lane groups that share a query row
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
 
-    // merge the 4 waves through LDS (the K/V staging area is free now)
+    // merge the 4 waves through LDS
     __syncthreads();
     float *ow = (float *)lds;  // [4 waves][16 rows][128 dv]
 #pragma unroll
@@ -237,9 +256,12 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
 #pragma unroll
     for (int br = 0; br < 2; ++br) {
         const int q = 2 * j + br;
+        // the splits' loads are independent: unrolled so they are in flight together
         float M = -INFINITY;
+#pragma unroll 8
         for (int s = 0; s < ns; ++s) M = fmaxf(M, base[((int64_t)s * p.qrows + q) * (kD + 2) + kD]);
         float acc = 0.0f, lsum = 0.0f;
+#pragma unroll 8
         for (int s = 0; s < ns; ++s) {
             const float *rq = base + ((int64_t)s * p.qrows + q) * (kD + 2);
             const float ms = rq[kD];

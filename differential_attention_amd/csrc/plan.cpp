@@ -185,7 +185,8 @@ int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::str
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: scale must be finite and >= 0");
     if (a->norm == DIFFATTN_NORM_RMS && !(a->eps > 0.0f && !isinf(a->eps)))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: eps must be finite and > 0");
-    if (a->split_pages < 0) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: split_pages must be >= 0");
+    if (a->split_pages < 0 || a->split_pages > 64)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: split_pages must be in [0, 64]");
     if ((int64_t)a->max_pages * a->page_size > (1 << 30))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: max_pages * page_size too large");
     if (a->dtype != DIFFATTN_BF16 || a->d_qk != 128 || a->d_v != 128 || a->page_size != 64)
@@ -206,7 +207,7 @@ int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::str
         sp = (int)((a->max_pages + want - 1) / want);
         sp = std::max(sp, 8);  // at least 512 tokens per item
     }
-    sp = std::min(sp, a->max_pages);
+    sp = std::min(std::min(sp, a->max_pages), 64);  // a split's page ids fit one wave
     plan->split_pages = sp;
     plan->num_splits = (a->max_pages + sp - 1) / sp;
     plan->qrows = 2 * group;

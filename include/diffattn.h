@@ -96,7 +96,7 @@ typedef struct {
  *   out         [B, H, d_v]                   strides so[0], so[1]
  * Supported: dtype DIFFATTN_BF16, d_qk == d_v == 128, page_size 64,
  * H / H_kv <= 8 query heads per KV head in each branch.
- * split_pages: pages per split-KV work item (0 = chosen by the library).
+ * split_pages: pages per split-KV work item, 0..64 (0 = chosen by the library).
  * dev_err: optional device int; bit 0 is OR-ed in when a page id outside
  * [0, num_pages) is met, bit 1 when a ctx_len is out of range. Such pages or
  * sequences are skipped (never read). NULL disables the report (the checks
