@@ -57,28 +57,36 @@ def decode_bytes(d):
     return kv + q + out + table
 
 
-def kernel_source_hash():
+# sources of the kernels each workload runs (their hash keys the stored counters)
+KERNEL_SOURCES = {
+    "prefill_v1": ["prefill_bf16.hip", "common.hpp"],
+    "prefill_v2": ["prefill_bf16.hip", "common.hpp"],
+    "longctx_v1": ["prefill_bf16.hip", "common.hpp"],
+    "decode_v2": ["decode.hip", "common.hpp"],
+}
+
+
+def kernel_source_hash(name):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "differential_attention_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in KERNEL_SOURCES.get(name, []):
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]
 
 
 def load_traffic(name):
-    """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel sources."""
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) from the
+    committed counter summary, or None if it was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    if name not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     try:
         with open(path) as f:
-            t = json.load(f)
-        e = t.get(name)
-        if e and e.get("source_hash") == kernel_source_hash():
+            e = json.load(f).get(name)
+        if e and e.get("source_hash") == kernel_source_hash(name):
             return e.get("bytes_per_launch")
-    except Exception:
+    except (OSError, ValueError):
         return None
     return None
 
