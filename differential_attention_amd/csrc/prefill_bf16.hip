@@ -13,17 +13,20 @@
 // max m, running sum l, unnormalised O) and the difference is taken once, in
 // fp32, in the epilogue.
 //
-// Work decomposition. One work-group = 4 waves = 128 query rows of one output
-// head; two work-groups share a CU (at most 128 VGPRs + 128 AGPRs per lane,
-// so two waves per SIMD interleave matrix-core and vector work).
-//  * Each wave owns 32 query rows. Its Q1/Q2 rows live in registers as MFMA B
-//    operands for the whole sweep; O1^T, O2^T (d_v x 32) live in AGPRs.
+// Work decomposition. A work-group owns 128 query rows of one output head,
+// in 32-row groups, one per wave or per pair of waves:
+//  * d_qk 64 (V1 shapes): 4 waves, each computes both branches of its 32 rows
+//    (256 unified registers a lane, two waves per SIMD, two work-groups a CU);
+//  * d_qk 128 (V2 shapes): 8 waves, waves 2r and 2r+1 own rows 32r..32r+31,
+//    the first for branch 1, the second for branch 2. Splitting the branches
+//    halves each wave's state (Q rows as MFMA B operands, one d_v x 32
+//    accumulator), so two waves share a SIMD where one wave holding both
+//    branches would not fit twice.
 //  * Key tiles of 64 keys stream HBM -> LDS with global_load_lds (16 bytes a
 //    lane, no register staging), double-buffered: the loads of tile t+1 are
 //    in flight while tile t is used. One key tile feeds both branches when
-//    K1 == K2 (V2); the value tile is loaded once and read once for both
-//    branches.
-//  * Per 32-key sub-block and branch: S^T = K Q^T (32 keys x 32 queries,
+//    K1 == K2 (V2); the value tile is loaded once for both branches.
+//  * Per 32-key sub-block: S^T = K Q^T (32 keys x 32 queries,
 //    v_mfma_f32_32x32x16_bf16), so a lane holds 16 scores of ONE query: the
 //    row max needs one v_permlane32_swap and the row sum stays lane-local
 //    until the end. The key order inside a sub-block is permuted when K rows
@@ -32,14 +35,18 @@
 //  * O^T += V^T P^T: the probabilities go straight from the S^T registers into
 //    the B operand; the V^T operand is read from the row-major V tile with
 //    ds_read_b64_tr_b16 (two reads give a lane 8 consecutive keys of one value
-//    column).
+//    column). The row sum accumulates the bf16 probabilities the product
+//    uses, two at a time (v_dot2_f32_bf16 against ones).
 //  * LDS tiles have no padding; 16-byte chunks are XOR-swizzled per row so the
 //    K-operand reads and the transposing V reads are free of bank conflicts.
-//  * Lazy rescale: a branch's reference max moves only when a block max
-//    exceeds it by 2^8, so the AGPR accumulators are rarely rescaled.
+//  * Lazy rescale: a wave's reference max moves only when a block max exceeds
+//    it by 2^8, so the accumulators are rarely rescaled.
 //  * Causal: key tiles past the work-group's last row are never loaded; a wave
 //    stops at its diagonal sub-block, the only one it masks (with the ragged
 //    end of the sequence). Work-groups with the longest rows run first.
+//  * Epilogue: y = O1 / l1 - lambda O2 / l2 (when the branches live in two
+//    waves, the branch-2 wave leaves lambda O2 / l2 in LDS for its partner),
+//    then the V1 norm, then one bf16 store.
 // Grid mapping: work-groups are dispatched round-robin over the 8 XCDs; when
 // the number of (batch, KV head) units is a multiple of 8, all work-groups
 // reading one KV head are placed on the same XCD so its K/V stay in that
@@ -60,6 +67,15 @@ constexpr int kBM = 128;              // query rows per work-group
 constexpr int kWM = 32;               // query rows per wave
 constexpr int kBN = 64;               // keys per LDS tile
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
+
+// branch-split decomposition for a head dimension (see the header comment)
+template <int DQK>
+struct Split {
+    static constexpr bool kOn = DQK == 128;
+    static constexpr int kThreads = kOn ? 512 : 256;
+    static constexpr int kNBr = kOn ? 1 : 2;  // branches per wave
+    static constexpr int kMinBlocks = kOn ? 1 : 2;
+};
 
 struct Bf16Params {
     const __bf16 *q1, *q2, *k1, *k2, *v;
@@ -98,25 +114,34 @@ __device__ __forceinline__ void wait_vmem_all() {
 
 template <int DQK, bool SHARED_K>
 struct Tile {
-    static constexpr int kKBytes = kBN * DQK * 2;             // one K tile
-    static constexpr int kVBytes = kBN * kDV * 2;             // the V tile
-    static constexpr int kNK = SHARED_K ? 1 : 2;              // K tiles per stage
-    static constexpr int kStage = kNK * kKBytes + kVBytes;    // bytes per stage
-    static constexpr int kKCh = DQK / 8;                      // 16-byte chunks per K row
-    static constexpr int kKLoads = kKBytes / 1024 / 4;        // 1 KB loads per wave per K tile
+    static constexpr int kKBytes = kBN * DQK * 2;           // one K tile
+    static constexpr int kVBytes = kBN * kDV * 2;           // the V tile
+    static constexpr int kNK = SHARED_K ? 1 : 2;            // K tiles per stage
+    static constexpr int kStage = kNK * kKBytes + kVBytes;  // bytes per stage
+    static constexpr int kKCh = DQK / 8;                    // 16-byte chunks per K row
+    static constexpr int kKBlocks = kNK * kKBytes / 1024;   // 1 KB blocks of K per stage
+    static constexpr int kBlocks = kStage / 1024;           // 1 KB blocks per stage
+    static constexpr int kRowsPerKBlock = 1024 / (2 * DQK);
 };
 
 template <int DQK, bool SHARED_K, bool NORM>
-__global__ __launch_bounds__(256, DQK == 64 ? 2 : 1) void prefill_bf16_kernel(Bf16Params p) {
+__global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void prefill_bf16_kernel(Bf16Params p) {
     using T = Tile<DQK, SHARED_K>;
-    constexpr int KC = DQK / 16;  // 16-wide k steps of the QK contraction
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * T::kStage];
+    using S = Split<DQK>;
+    constexpr int KC = DQK / 16;           // 16-wide k steps of the QK contraction
+    constexpr int NBR = S::kNBr;           // branches computed by one wave
+    constexpr int NW = S::kThreads / 64;   // waves per work-group
+    // with split branches the epilogue reuses the stages for 4 waves x 64 lanes x 64 floats
+    constexpr int kLdsBytes = (S::kOn && 2 * T::kStage < 65536) ? 65536 : 2 * T::kStage;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
+    const int br0 = S::kOn ? (wave & 1) : 0;   // first branch of this wave (0: Q1/K1, 1: Q2/K2)
+    const int rg = S::kOn ? (wave >> 1) : wave;  // row group
 
     // ---- which (batch, head, row block) this work-group computes
     int b, h, rb;
@@ -144,19 +169,19 @@ __global__ __launch_bounds__(256, DQK == 64 ? 2 : 1) void prefill_bf16_kernel(Bf
     }
     const int g = h / p.group;
     const int q0 = rb * kBM;
-    const int wrow0 = q0 + wave * kWM;  // first query row of this wave
-    const int myrow = wrow0 + l32;      // the query row of this lane
+    const int wrow0 = q0 + rg * kWM;  // first query row of this wave
+    const int myrow = wrow0 + l32;    // the query row of this lane
 
-    // ---- Q fragments (B operands): lane holds Q[myrow][16 kc + 8 hh .. +7]
-    bf16x8 qf1[KC], qf2[KC];
+    // ---- Q fragments of this wave's branches (B operands): Q[myrow][16 kc + 8 hh .. +7]
+    bf16x8 qf[NBR][KC];
     {
         const int row = min(myrow, p.N - 1);  // rows past the end compute garbage, never stored
-        const __bf16 *q1 = p.q1 + b * p.sq1[0] + h * p.sq1[1] + (int64_t)row * p.sq1[2] + 8 * hh;
-        const __bf16 *q2 = p.q2 + b * p.sq2[0] + h * p.sq2[1] + (int64_t)row * p.sq2[2] + 8 * hh;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            qf1[kc] = as_bf16x8(ldg16(q1 + 16 * kc));
-            qf2[kc] = as_bf16x8(ldg16(q2 + 16 * kc));
+        for (int j = 0; j < NBR; ++j) {
+            const __bf16 *q = (br0 + j) ? p.q2 + b * p.sq2[0] + h * p.sq2[1] + (int64_t)row * p.sq2[2]
+                                        : p.q1 + b * p.sq1[0] + h * p.sq1[1] + (int64_t)row * p.sq1[2];
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) qf[j][kc] = as_bf16x8(ldg16(q + 8 * hh + 16 * kc));
         }
     }
 
@@ -171,47 +196,46 @@ __global__ __launch_bounds__(256, DQK == 64 ? 2 : 1) void prefill_bf16_kernel(Bf
     const int wend = p.causal ? min(p.N, wrow0 + kWM) : p.N;
     const int nsub = wrow0 < p.N ? (wend + 31) / 32 : 0;
 
-    // ---- per-lane constants of the global -> LDS copies. Load i of wave w
-    // fills the 1 KB block (4 i + w) of a region; lane l fills its 16-byte
-    // slot l. Slot -> (row, physical chunk) -> logical chunk via the swizzle.
-    // K (DQK 128): 16 chunks a row, 4 rows per block; (DQK 64): 8 chunks, 8 rows.
-    constexpr int kRowsPerBlock = 1024 / (2 * DQK);
-    const int k_row_l = lane / T::kKCh;                        // row inside the block
-    const int k_pc = lane % T::kKCh;                            // physical chunk
-    const int k_col = 8 * (k_pc ^ k_swz<DQK>(wave * kRowsPerBlock + k_row_l));
-    const int v_row_l = lane >> 4;
-    const int v_col = 8 * ((lane & 15) ^ v_swz(v_row_l));
-
+    // ---- global -> LDS copies: 1 KB block B of a stage is filled by wave
+    // B % NW (load B / NW), lane l filling 16-byte slot l; blocks [0, kKBlocks)
+    // hold the K tile(s), the rest the V tile. Slot -> (row, physical chunk)
+    // -> logical chunk through the row's swizzle.
+    static_assert(T::kBlocks % NW == 0, "stage blocks must divide among the waves");
     auto issue_tile = [&](int t, int stage) {
         const int key0 = t * kBN;
         unsigned char *base = lds + stage * T::kStage;
 #pragma unroll
-        for (int i = 0; i < T::kKLoads; ++i) {
-            const int blk = 4 * i + wave;
-            const int key = min(key0 + blk * kRowsPerBlock + k_row_l, p.N - 1);
-            __builtin_amdgcn_global_load_lds(kb1 + (int64_t)key * sk1n + k_col,
-                                             (lds_void *)(base + blk * 1024), 16, 0, 0);
-            if constexpr (!SHARED_K)
-                __builtin_amdgcn_global_load_lds(kb2 + (int64_t)key * sk2n + k_col,
-                                                 (lds_void *)(base + T::kKBytes + blk * 1024), 16, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int blk = 4 * i + wave;
-            const int key = min(key0 + blk * 4 + v_row_l, p.N - 1);
-            __builtin_amdgcn_global_load_lds(vb + (int64_t)key * svn + v_col,
-                                             (lds_void *)(base + T::kNK * T::kKBytes + blk * 1024), 16, 0, 0);
+        for (int i = 0; i < T::kBlocks / NW; ++i) {
+            const int blk = wave + NW * i;
+            if (blk < T::kKBlocks) {
+                const int kt = blk / (T::kKBytes / 1024);  // which K tile (0: K1, 1: K2)
+                const int kblk = blk % (T::kKBytes / 1024);
+                const int row = kblk * T::kRowsPerKBlock + lane / T::kKCh;
+                const int col = 8 * ((lane % T::kKCh) ^ k_swz<DQK>(row));
+                const int key = min(key0 + row, p.N - 1);
+                const __bf16 *src = (kt ? kb2 + (int64_t)key * sk2n : kb1 + (int64_t)key * sk1n) + col;
+                __builtin_amdgcn_global_load_lds(src, (lds_void *)(base + blk * 1024), 16, 0, 0);
+            } else {
+                const int vblk = blk - T::kKBlocks;
+                const int row = vblk * 4 + (lane >> 4);
+                const int col = 8 * ((lane & 15) ^ v_swz(row));
+                const int key = min(key0 + row, p.N - 1);
+                __builtin_amdgcn_global_load_lds(vb + (int64_t)key * svn + col,
+                                                 (lds_void *)(base + blk * 1024), 16, 0, 0);
+            }
         }
     };
 
-    // ---- per-branch online-softmax state
-    f32x16 o1[4], o2[4];
+    // ---- online-softmax state of this wave's branches
+    f32x16 o[NBR][4];
+    float m[NBR], l[NBR];
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-        o1[dc] = f32x16{};
-        o2[dc] = f32x16{};
+    for (int j = 0; j < NBR; ++j) {
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc) o[j][dc] = f32x16{};
+        m[j] = -INFINITY;
+        l[j] = 0.0f;
     }
-    float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.0f, l2 = 0.0f;
 
     // byte offset of this lane's K-operand chunk for k step kc, sub-block sb
     const int krow = perm_key(l32);
@@ -220,8 +244,9 @@ __global__ __launch_bounds__(256, DQK == 64 ? 2 : 1) void prefill_bf16_kernel(Bf
         const int c = (2 * kc + hh) ^ k_swz<DQK>(row);
         return row * (2 * DQK) + 16 * c;
     };
-    // byte offsets of this lane's two transposing V reads for (sb, k step t, dv block dc)
-    const int vi = lane & 15;           // lane inside its 16-lane group
+    // byte offset of one of this lane's two transposing V reads for
+    // (sub-block sb, k step t, dv block dc, half)
+    const int vi = lane & 15;  // lane inside its 16-lane group
     const int vdv0 = 16 * ((lane >> 4) & 1);
     auto v_addr = [&](int sb, int t, int dc, int half) {
         const int row = 32 * sb + 16 * t + 8 * hh + 4 * half + (vi >> 2);
@@ -229,66 +254,74 @@ __global__ __launch_bounds__(256, DQK == 64 ? 2 : 1) void prefill_bf16_kernel(Bf
         const int c = (col >> 3) ^ v_swz(row);
         return row * 256 + 16 * c + 2 * (col & 7);
     };
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // scores of one branch for one sub-block, masked when `mask`
-    auto scores = [&](const unsigned char *ktile, const bf16x8 *qf, int sb, bool mask, int lim) {
+    // one branch of one sub-block: scores, online softmax (reference max moved
+    // lazily), bf16 probabilities for the two 16-key steps
+    auto softmax_branch = [&](const unsigned char *kt, const bf16x8 *q, int sb, bool mask, int lim, float &mr,
+                              float &lr, f32x16 *orr, bf16x8 &pb0, bf16x8 &pb1) {
         f32x16 s = f32x16{};
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-            s = mfma32(as_bf16x8(*(const uint4 *)(ktile + k_addr(sb, kc))), qf[kc], s);
+        for (int kc = 0; kc < KC; ++kc) s = mfma32(as_bf16x8(*(const uint4 *)(kt + k_addr(sb, kc))), q[kc], s);
         if (mask) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (key_of_reg(r) >= lim) s[r] = -INFINITY;
         }
-        return s;
-    };
-    // online softmax of one branch: returns the bf16 probabilities for the two
-    // 16-key steps, updates (m, l) and rescales o when the reference max moves
-    auto softmax = [&](f32x16 s, float &m, float &l, f32x16 *o, bf16x8 &pb0, bf16x8 &pb1) {
         float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
         for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
         mx = fmaxf(mx, s[15]);
         const float mxs = halves_max(mx) * p.sc_log2;
-        if (__any(mxs > m + kRescaleLog2)) {
-            const float mnew = fmaxf(m, mxs);
-            const float alpha = (m == mnew) ? 1.0f : exp2_fast(m - mnew);
-            m = mnew;
-            l *= alpha;
+        if (__any(mxs > mr + kRescaleLog2)) {
+            const float mnew = fmaxf(mr, mxs);
+            const float alpha = (mr == mnew) ? 1.0f : exp2_fast(mr - mnew);
+            mr = mnew;
+            lr *= alpha;
 #pragma unroll
-            for (int dc = 0; dc < 4; ++dc) o[dc] *= alpha;
+            for (int dc = 0; dc < 4; ++dc) orr[dc] *= alpha;
         }
-        const float msub = (m == -INFINITY) ? 0.0f : m;
-        float ps[16];
+        const float msub = (mr == -INFINITY) ? 0.0f : mr;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ps[r] = exp2_fast(fmaf(s[r], p.sc_log2, -msub));
-        float a0 = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-        float a1 = (ps[4] + ps[5]) + (ps[6] + ps[7]);
-        float a2 = (ps[8] + ps[9]) + (ps[10] + ps[11]);
-        float a3 = (ps[12] + ps[13]) + (ps[14] + ps[15]);
-        l += (a0 + a1) + (a2 + a3);
-        pb0 = pack8(ps[0], ps[1], ps[2], ps[3], ps[4], ps[5], ps[6], ps[7]);
-        pb1 = pack8(ps[8], ps[9], ps[10], ps[11], ps[12], ps[13], ps[14], ps[15]);
+        for (int r = 0; r < 16; ++r) s[r] = exp2_fast(fmaf(s[r], p.sc_log2, -msub));
+        bf16x2 pp[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pp[i] = pack2(s[2 * i], s[2 * i + 1]);
+        // row sum of the rounded probabilities the product uses
+        float l0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], ones, 0.0f, false);
+        float l1 = __builtin_amdgcn_fdot2_f32_bf16(pp[4], ones, 0.0f, false);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+            l0 = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l0, false);
+            l1 = __builtin_amdgcn_fdot2_f32_bf16(pp[4 + i], ones, l1, false);
+        }
+        lr += l0 + l1;
+        pb0 = bf16x8{pp[0][0], pp[0][1], pp[1][0], pp[1][1], pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
+        pb1 = bf16x8{pp[4][0], pp[4][1], pp[5][0], pp[5][1], pp[6][0], pp[6][1], pp[7][0], pp[7][1]};
     };
 
     auto step = [&](const unsigned char *base, int sb, bool mask, int lim) {
-        const unsigned char *kt1 = base;
-        const unsigned char *kt2 = SHARED_K ? base : base + T::kKBytes;
         const unsigned char *vt = base + T::kNK * T::kKBytes;
-        bf16x8 p10, p11, p20, p21;
-        softmax(scores(kt1, qf1, sb, mask, lim), m1, l1, o1, p10, p11);
-        softmax(scores(kt2, qf2, sb, mask, lim), m2, l2, o2, p20, p21);
+        bf16x8 pb[NBR][2];
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) {
+        for (int j = 0; j < NBR; ++j) {
+            const unsigned char *kt = base + (SHARED_K ? 0 : (br0 + j) * T::kKBytes);
+            softmax_branch(kt, qf[j], sb, mask, lim, m[j], l[j], o[j], pb[j][0], pb[j][1]);
+        }
+        // O^T += V^T P^T, one V read for every branch of the wave; the next
+        // step's V operand is read while this step's products run
+        auto vfrag = [&](int i) {  // step i = (dv block i / 2, k step i % 2)
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, i & 1, i >> 1, 0)));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, i & 1, i >> 1, 1)));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 va = vfrag(0);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, t, dc, 0)));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, t, dc, 1)));
-                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o1[dc] = mfma32(va, t ? p11 : p10, o1[dc]);
-                o2[dc] = mfma32(va, t ? p21 : p20, o2[dc]);
-            }
+        for (int i = 0; i < 8; ++i) {
+            const bf16x8 vn = i + 1 < 8 ? vfrag(i + 1) : va;
+#pragma unroll
+            for (int j = 0; j < NBR; ++j) o[j][i >> 1] = mfma32(va, pb[j][i & 1], o[j][i >> 1]);
+            va = vn;
         }
     };
 
@@ -314,17 +347,52 @@ __global__ __launch_bounds__(256, DQK == 64 ? 2 : 1) void prefill_bf16_kernel(Bf
     }
 
     // ---- epilogue: y = O1 / l1 - lambda O2 / l2 (then the V1 norm), bf16 store
-    l1 = halves_sum(l1);
-    l2 = halves_sum(l2);
-    const float r1 = 1.0f / l1;
-    const float r2 = p.lambda[h] / l2;
-    f32x16 y[4];
-    {
-        // both products rounded separately (no fused multiply-add), so identical
-        // branches with lambda = 1 give exactly zero
-#pragma clang fp contract(off)
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) y[dc] = o1[dc] * r1 - o2[dc] * r2;
+    for (int j = 0; j < NBR; ++j) l[j] = halves_sum(l[j]);
+    f32x16 y[4];
+    if constexpr (S::kOn) {
+        // branch-2 waves hand lambda O2 / l2 to their branch-1 partner through LDS
+        __syncthreads();  // every wave is done with the key tiles
+        float *xch = (float *)lds + ((rg * 64 + lane) * 64);  // this lane's 64 values
+        if (br0) {
+            const float r2 = p.lambda[h] / l[0];
+#pragma unroll
+            for (int dc = 0; dc < 4; ++dc) {
+                const f32x16 w = o[0][dc] * r2;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v4 = {w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+                    *(float4 *)(xch + 16 * dc + 4 * q) = v4;
+                }
+            }
+        }
+        __syncthreads();
+        if (br0) return;
+        const float r1 = 1.0f / l[0];
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc) {
+            // both products rounded separately (no fused multiply-add), so identical
+            // branches with lambda = 1 give exactly zero
+#pragma clang fp contract(off)
+            f32x16 w2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v4 = *(const float4 *)(xch + 16 * dc + 4 * q);
+                w2[4 * q] = v4.x;
+                w2[4 * q + 1] = v4.y;
+                w2[4 * q + 2] = v4.z;
+                w2[4 * q + 3] = v4.w;
+            }
+            y[dc] = o[0][dc] * r1 - w2;
+        }
+    } else {
+        const float r1 = 1.0f / l[0];
+        const float r2 = p.lambda[h] / l[NBR - 1];
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc) {
+#pragma clang fp contract(off)
+            y[dc] = o[0][dc] * r1 - o[NBR - 1][dc] * r2;
+        }
     }
     if constexpr (NORM) {
         float ss = 0.0f;
@@ -356,7 +424,8 @@ __global__ __launch_bounds__(256, DQK == 64 ? 2 : 1) void prefill_bf16_kernel(Bf
 
 template <int DQK, bool SHARED_K, bool NORM>
 hipError_t launch_t(const Bf16Params &p, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<DQK, SHARED_K, NORM>), dim3(blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<DQK, SHARED_K, NORM>), dim3(blocks), dim3(Split<DQK>::kThreads), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
