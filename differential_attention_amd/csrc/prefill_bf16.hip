@@ -310,9 +310,17 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         }
         // O^T += V^T P^T, one V read for every branch of the wave; the next
         // step's V operand is read while this step's products run
-        auto vfrag = [&](int i) {  // step i = (dv block i / 2, k step i % 2)
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, i & 1, i >> 1, 0)));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, i & 1, i >> 1, 1)));
+        // step i covers (k step t, dv block dc). With one branch per wave the k
+        // step is the outer index, so the 4 accumulators of a k step are updated
+        // back to back and dependent products sit 4 apart; with two branches the
+        // dv block is outer (the two branches' products already alternate), which
+        // keeps the register footprint of the two-branch wave within budget.
+        constexpr bool kStepOuter = NBR == 1;
+        auto t_of = [](int i) { return kStepOuter ? (i >> 2) : (i & 1); };
+        auto dc_of = [](int i) { return kStepOuter ? (i & 3) : (i >> 1); };
+        auto vfrag = [&](int i) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, t_of(i), dc_of(i), 0)));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, t_of(i), dc_of(i), 1)));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         bf16x8 va = vfrag(0);
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         for (int i = 0; i < 8; ++i) {
             const bf16x8 vn = i + 1 < 8 ? vfrag(i + 1) : va;
 #pragma unroll
-            for (int j = 0; j < NBR; ++j) o[j][i >> 1] = mfma32(va, pb[j][i & 1], o[j][i >> 1]);
+            for (int j = 0; j < NBR; ++j) o[j][dc_of(i)] = mfma32(va, pb[j][t_of(i)], o[j][dc_of(i)]);
             va = vn;
         }
     };
