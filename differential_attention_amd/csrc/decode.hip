@@ -3,13 +3,27 @@
 // are doubled, the KV heads stay, so the KV cache is loaded once per step and
 // every key/value byte feeds all query heads of its group, both branches).
 //
-// Pass 1 (decode_split_kernel), one work-group per (split s, KV head g,
-// sequence b). All 2 * group query rows of the KV head (both branches of
+// Work decomposition. The (sequence, KV head) units, in order, with their
+// pages form one global page list of T pages. Pass 1 (decode_split_kernel)
+// gives work-group w the contiguous range [w T / W, (w + 1) T / W) of it, so
+// every work-group streams the same number of pages whatever the mix of
+// sequence lengths (no tail of long items); W is one round of resident
+// work-groups unless the caller asks for a page count per work-group. A
+// range can start and end inside a unit and can cross several; for each
+// unit u it touches, work-group w writes one partial state to record w + u
+// of the workspace (unique: a later work-group never touches an earlier
+// unit). Pass 2 (decode_combine_kernel), one work-group per (output head,
+// sequence), finds the work-groups that covered its unit from the same
+// arithmetic and merges their records with the log-sum-exp rule, forms
+// y = O1 - lambda O2 and, for the V1 norm, y / sqrt(mean(y^2) + eps) *
+// gamma * (1 - lambda_init).
+//
+// Inside a range, all 2 * group query rows of the KV head (both branches of
 // every pair) form one 16-column MFMA operand, so each K and V byte is read
 // from HBM exactly once. Each of the 4 waves owns a 16-token slice of every
-// page of the split and streams it independently -- no barrier inside the
-// page loop: the next kBuf pages' K and V slices are loaded into registers
-// while the current one is used, so every wave keeps HBM requests in flight.
+// page and streams it independently -- no barrier inside the page loop: the
+// next kBuf pages' K and V slices are loaded into registers while the current
+// one is used, so every wave keeps HBM requests in flight.
 //   S^T = K Q^T      16 tokens x 16 query rows, v_mfma_f32_16x16x32_bf16;
 //                    each lane loads its K operand (token, 8 features)
 //                    straight from HBM in MFMA operand layout
@@ -19,19 +33,20 @@
 //                    a wave-private LDS buffer (XOR-swizzled rows) and
 //                    ds_read_b64_tr_b16 returns 4 consecutive tokens of one
 //                    value column
-// At the end the 4 waves' states are merged through LDS and the split's
-// (max, sum, unnormalised O) per query row is written to the workspace.
-// Pass 2 (decode_combine_kernel), one work-group per (output head, sequence):
-// merges the splits of each branch with the log-sum-exp rule, forms
-// y = O1 - lambda O2 and, for the V1 norm, y / sqrt(mean(y^2) + eps) *
-// gamma * (1 - lambda_init).
+// At the end of a unit's part the 4 waves' states are merged through LDS and
+// the (max, sum, unnormalised O) of each query row is written to its record.
 // Token t of sequence b is slot t % 64 of page page_table[b][t / 64]; tokens
 // at or past ctx_len[b] are masked and their value rows replaced by zeros, so
 // whatever an unused cache slot holds cannot reach the output. A page id
 // outside [0, num_pages) is never dereferenced: page 0 is read in its place,
-// all its tokens are masked and bit 0 of *dev_err is set.
+// all its tokens are masked and bit 0 of *dev_err is set. A sequence whose
+// length is out of range has no pages; its outputs are zeros and bit 1 of
+// *dev_err is set.
 #include "common.hpp"
 #include "launch.hpp"
+
+#include <algorithm>
+#include <atomic>
 
 namespace da {
 
@@ -47,6 +62,10 @@ constexpr int kPage = 64;    // tokens per page
 #define DIFFATTN_DECODE_KBUF 2
 #endif
 constexpr int kBuf = DIFFATTN_DECODE_KBUF;  // pages of K/V held in registers per wave
+#ifndef DIFFATTN_DECODE_ROUNDS
+#define DIFFATTN_DECODE_ROUNDS 1
+#endif
+constexpr int kRounds = DIFFATTN_DECODE_ROUNDS;  // rounds of resident work-groups (library's choice)
 
 struct DecodeParams {
     const __bf16 *q1, *q2;
@@ -56,13 +75,55 @@ struct DecodeParams {
     const float *lambda, *gamma;
     __bf16 *out;
     int64_t so[2];
-    float *ws;
+    int32_t *pref;  // workspace header: pages of the valid sequences before b, [B + 1]
+    float *rec;     // workspace records, qrows * (kD + 2) floats each
     int *dev_err;
-    int H, H_kv, group, qrows, max_pages, num_pages, split_pages, num_splits, norm;
+    int B, H, H_kv, group, qrows, max_pages, num_pages, target, num_wgs, norm;
     float sc_log2, eps, one_minus_init;
 };
 
 __device__ __forceinline__ uint4 ldg16(const __bf16 *p) { return *(const uint4 *)p; }
+
+// pages of sequence b; 0 for b >= B or a length out of range
+__device__ __forceinline__ int seq_pages(const DecodeParams &p, int b) {
+    if (b >= p.B) return 0;
+    const int L = p.ctx_len[b];
+    return (L >= 1 && L <= p.max_pages * kPage) ? (L + kPage - 1) / kPage : 0;
+}
+
+// work-groups that share the T pages (each gets at least one)
+__device__ __forceinline__ int64_t active_wgs(const DecodeParams &p, int64_t T) {
+    if (T <= 0) return 0;
+    const int64_t want = p.target > 0 ? (T + p.target - 1) / p.target : T / kDecodeMinPages;
+    return min((int64_t)p.num_wgs, max((int64_t)1, want));
+}
+
+// sum over the 256 threads of a work-group
+__device__ __forceinline__ int block_sum(int x, int *sh) {
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    const int t = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();
+    return t;
+}
+
+// inclusive prefix sum over the 256 threads of a work-group; *total = the sum
+__device__ __forceinline__ int block_scan(int x, int *sh, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(x, o, 64);
+        if (lane >= o) x += t;
+    }
+    if (lane == 63) sh[wave] = x;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) before += i < wave ? sh[i] : 0;
+    *total = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();
+    return x + before;
+}
 
 // one wave's 16-token slice of a page: K operands and V rows
 struct Slice {
@@ -74,60 +135,46 @@ struct Slice {
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * 16 * kD * 4];  // 32 KB
     __shared__ float red_m[4][16], red_l[4][16];
+    __shared__ int sh[4], s_b, s_excl;
 
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int w = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, grp = lane >> 4;
 
-    const int L = p.ctx_len[b];
-    if (L < 1 || L > p.max_pages * kPage) {
-        if (tid == 0 && s == 0 && g == 0 && p.dev_err) atomicOr(p.dev_err, 2);
-        return;
-    }
-    const int npages = (L + kPage - 1) / kPage;
-    const int pb = s * p.split_pages;
-    const int pe = min(npages, pb + p.split_pages);
-    if (pb >= pe) return;
-    const int np = pe - pb;
+    // the global page list: T pages, W work-groups share it
+    int part = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 256) part += seq_pages(p, b0 + tid);
+    const int tseq = block_sum(part, sh);
+    const int64_t T = (int64_t)tseq * p.H_kv;
+    const int64_t W = active_wgs(p, T);
+    if (w >= W && w != 0) return;
+    const int64_t start = W > 0 ? (int64_t)w * T / W : 0;
+    const int64_t end = W > 0 ? (int64_t)(w + 1) * T / W : 0;
 
-    // Q^T fragments: lane supplies query row n, d = 32 kc + 8 grp .. +7
-    bf16x8 qf[4];
-    {
-        const bool ok = n < p.qrows;
-        const int pair = n >> 1, br = n & 1;
-        const int h = g * p.group + (ok ? pair : 0);
-        const __bf16 *q = br ? p.q2 + b * p.sq2[0] + h * p.sq2[1] : p.q1 + b * p.sq1[0] + h * p.sq1[1];
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            uint4 z = {0u, 0u, 0u, 0u};
-            qf[kc] = as_bf16x8(ok ? ldg16(q + 32 * kc + 8 * grp) : z);
+    // find the unit holding page `start` (a prefix sum over the sequences);
+    // work-group 0 also stores the prefix for the combine pass
+    int carry = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 256) {
+        const int bb = b0 + tid;
+        const int c = seq_pages(p, bb);
+        int tot;
+        const int excl = carry + block_scan(c, sh, &tot) - c;
+        if (w == 0 && bb < p.B) p.pref[bb] = excl;
+        if (c > 0 && (int64_t)excl * p.H_kv <= start && start < (int64_t)(excl + c) * p.H_kv) {
+            s_b = bb;
+            s_excl = excl;
         }
+        carry += tot;
     }
+    if (w == 0 && tid == 0) p.pref[p.B] = carry;
+    if (w >= W) return;
+    __syncthreads();
 
-    // the split's page ids (at most 64), one per lane, read once; each page's id
-    // is then taken with v_readlane (a scalar), so no vector load of the table
-    // sits between the K/V loads of consecutive pages
-    const int32_t *table = p.page_table + (int64_t)b * p.max_pages;
-    const int ids = lane < np ? table[pb + lane] : 0;
-    bool bad_page = false;
-    auto load = [&](Slice &S, int k) {
-        int phys = __builtin_amdgcn_readlane(ids, k);
-        S.ok = phys >= 0 && phys < p.num_pages;
-        bad_page |= !S.ok;
-        phys = S.ok ? phys : 0;
-        const int64_t base = (((int64_t)phys * p.H_kv + g) * kPage + 16 * wave) * kD;
-        const __bf16 *kp = p.kc + base + n * kD + 8 * grp;
-        const __bf16 *vp = p.vc + base + grp * kD + 8 * n;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) S.k[kc] = ldg16(kp + 32 * kc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S.v[i] = ldg16(vp + 4 * i * kD);
-    };
-
-    f32x4 o[8];
-#pragma unroll
-    for (int dc = 0; dc < 8; ++dc) o[dc] = f32x4{};
-    float m = -INFINITY, l = 0.0f;
+    int b = __builtin_amdgcn_readfirstlane(s_b);
+    int c = seq_pages(p, b);
+    int64_t ubase = (int64_t)__builtin_amdgcn_readfirstlane(s_excl) * p.H_kv;  // first page of unit (b, g)
+    int g = (int)((start - ubase) / c);
+    ubase += (int64_t)g * c;
 
     // this wave's V buffer: 16 rows x 256 bytes, 16-byte chunks XOR-swizzled
     // by 2 (row & 7) so each transposing read pass touches 64 distinct banks
@@ -135,107 +182,172 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int vrow = 4 * grp + (n >> 2);  // row this lane addresses in a transposing read
     const int vswz = (vrow & 7) << 1;
 
-    auto process = [&](const Slice &S, int k) {
-        const int pg = pb + k;
-        const int vis = L - pg * kPage - 16 * wave;  // visible rows of this slice
-        // V rows into the wave buffer (rows past the end as zeros)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 4 * i + grp;
-            const uint32_t keep = row < vis ? 0xffffffffu : 0u;  // select by value, not by address
-            uint4 v = S.v[i];
-            v.x &= keep;
-            v.y &= keep;
-            v.z &= keep;
-            v.w &= keep;
-            *(uint4 *)(vbuf + row * 256 + 16 * (n ^ ((row & 7) << 1))) = v;
-        }
-        // scores of the 16 tokens against the 16 query rows
-        f32x4 sc = f32x4{};
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) sc = mfma16(as_bf16x8(S.k[kc]), qf[kc], sc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (!S.ok || 4 * grp + r >= vis) sc[r] = -INFINITY;
-        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m, mx * p.sc_log2);
-        const float alpha = (m == mnew) ? 1.0f : exp2_fast(m - mnew);
-        const float msub = (mnew == -INFINITY) ? 0.0f : mnew;
-        m = mnew;
-        float pr[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(fmaf(sc[r], p.sc_log2, -msub));
-        l = l * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
-#pragma unroll
-        for (int dc = 0; dc < 8; ++dc) o[dc] *= alpha;
-        const bf16x2 p01 = pack2(pr[0], pr[1]), p23 = pack2(pr[2], pr[3]);
-        const bf16x4_t pb4 = {p01[0], p01[1], p23[0], p23[1]};
-        // the V rows written above must be complete before other lanes read them
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        const unsigned char *vr = vbuf + vrow * 256;
-#pragma unroll
-        for (int dc = 0; dc < 8; ++dc) {
-            const int col = 16 * dc + 4 * (n & 3);
-            const int c = (col >> 3) ^ vswz;
-            const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 16 * c + 2 * (col & 7)));
-            o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, va), pb4, o[dc], 0, 0, 0);
-        }
-        // the reads must be complete before the next slice overwrites the buffer
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-    };
+    for (int64_t pos = start;;) {
+        // pages [p0, p1) of unit (b, g)
+        const int p0 = (int)(pos - ubase);
+        const int p1 = (int)(min(end, ubase + c) - ubase);
+        const int L = p.ctx_len[b];
 
-    Slice S[kBuf];
+        // Q^T fragments: lane supplies query row n, d = 32 kc + 8 grp .. +7
+        bf16x8 qf[4];
+        {
+            const bool ok = n < p.qrows;
+            const int pair = n >> 1, br = n & 1;
+            const int h = g * p.group + (ok ? pair : 0);
+            const __bf16 *q = br ? p.q2 + b * p.sq2[0] + h * p.sq2[1] : p.q1 + b * p.sq1[0] + h * p.sq1[1];
 #pragma unroll
-    for (int j = 0; j < kBuf; ++j)
-        if (j < np) load(S[j], j);
-    for (int k0 = 0; k0 < np; k0 += kBuf) {
-#pragma unroll
-        for (int j = 0; j < kBuf; ++j) {
-            const int k = k0 + j;
-            if (k < np) {
-                process(S[j], k);
-                if (k + kBuf < np) load(S[j], k + kBuf);
+            for (int kc = 0; kc < 4; ++kc) {
+                uint4 z = {0u, 0u, 0u, 0u};
+                qf[kc] = as_bf16x8(ok ? ldg16(q + 32 * kc + 8 * grp) : z);
             }
         }
-    }
-    if (bad_page && lane == 0 && p.dev_err) atomicOr(p.dev_err, 1);
 
-    // row sums over the 4 lane groups that share a query row
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+        f32x4 o[8];
+#pragma unroll
+        for (int dc = 0; dc < 8; ++dc) o[dc] = f32x4{};
+        float m = -INFINITY, l = 0.0f;
+        bool bad_page = false;
 
-    // merge the 4 waves through LDS
-    __syncthreads();
-    float *ow = (float *)lds;  // [4 waves][16 rows][128 dv]
+        // pages in chunks of at most 64: a chunk's page ids are read once, one
+        // per lane, and each page's id is then taken with v_readlane (a scalar),
+        // so no vector load of the table sits between the K/V loads of pages
+        const int32_t *table = p.page_table + (int64_t)b * p.max_pages;
+        for (int c0 = p0; c0 < p1; c0 += 64) {
+            const int np = min(64, p1 - c0);
+            const int ids = lane < np ? table[c0 + lane] : 0;
+            auto load = [&](Slice &S, int k) {
+                int phys = __builtin_amdgcn_readlane(ids, k);
+                S.ok = phys >= 0 && phys < p.num_pages;
+                bad_page |= !S.ok;
+                phys = S.ok ? phys : 0;
+                const int64_t base = (((int64_t)phys * p.H_kv + g) * kPage + 16 * wave) * kD;
+                const __bf16 *kp = p.kc + base + n * kD + 8 * grp;
+                const __bf16 *vp = p.vc + base + grp * kD + 8 * n;
 #pragma unroll
-    for (int dc = 0; dc < 8; ++dc)
+                for (int kc = 0; kc < 4; ++kc) S.k[kc] = ldg16(kp + 32 * kc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ow[(wave * 16 + n) * kD + 16 * dc + 4 * grp + r] = o[dc][r];
-    if (grp == 0) {
-        red_m[wave][n] = m;
-        red_l[wave][n] = l;
-    }
-    __syncthreads();
-    float *rec = p.ws + (((int64_t)b * p.H_kv + g) * p.num_splits + s) * p.qrows * (kD + 2);
-    for (int idx = tid; idx < p.qrows * kD; idx += 256) {
-        const int q = idx / kD, dv = idx % kD;
-        float M = fmaxf(fmaxf(red_m[0][q], red_m[1][q]), fmaxf(red_m[2][q], red_m[3][q]));
-        float acc = 0.0f, lsum = 0.0f;
+                for (int i = 0; i < 4; ++i) S.v[i] = ldg16(vp + 4 * i * kD);
+            };
+
+            auto process = [&](const Slice &S, int k) {
+                const int pg = c0 + k;
+                const int vis = L - pg * kPage - 16 * wave;  // visible rows of this slice
+                // V rows into the wave buffer (rows past the end as zeros)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float mw = red_m[w][q];
-            const float f = (mw == -INFINITY) ? 0.0f : exp2_fast(mw - M);
-            acc += ow[(w * 16 + q) * kD + dv] * f;
-            lsum += red_l[w][q] * f;
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * i + grp;
+                    const uint32_t keep = row < vis ? 0xffffffffu : 0u;  // select by value, not by address
+                    uint4 v = S.v[i];
+                    v.x &= keep;
+                    v.y &= keep;
+                    v.z &= keep;
+                    v.w &= keep;
+                    *(uint4 *)(vbuf + row * 256 + 16 * (n ^ ((row & 7) << 1))) = v;
+                }
+                // scores of the 16 tokens against the 16 query rows
+                f32x4 sc = f32x4{};
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) sc = mfma16(as_bf16x8(S.k[kc]), qf[kc], sc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (!S.ok || 4 * grp + r >= vis) sc[r] = -INFINITY;
+                float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float mnew = fmaxf(m, mx * p.sc_log2);
+                const float alpha = (m == mnew) ? 1.0f : exp2_fast(m - mnew);
+                const float msub = (mnew == -INFINITY) ? 0.0f : mnew;
+                m = mnew;
+                float pr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(fmaf(sc[r], p.sc_log2, -msub));
+                l = l * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+                for (int dc = 0; dc < 8; ++dc) o[dc] *= alpha;
+                const bf16x2 p01 = pack2(pr[0], pr[1]), p23 = pack2(pr[2], pr[3]);
+                const bf16x4_t pb4 = {p01[0], p01[1], p23[0], p23[1]};
+                // the V rows written above must be complete before other lanes read them
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                const unsigned char *vr = vbuf + vrow * 256;
+#pragma unroll
+                for (int dc = 0; dc < 8; ++dc) {
+                    const int col = 16 * dc + 4 * (n & 3);
+                    const int cc = (col >> 3) ^ vswz;
+                    const s16x4 va =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 16 * cc + 2 * (col & 7)));
+                    o[dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, va), pb4,
+                                                                      o[dc], 0, 0, 0);
+                }
+                // the reads must be complete before the next slice overwrites the buffer
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+            };
+
+            Slice S[kBuf];
+#pragma unroll
+            for (int j = 0; j < kBuf; ++j)
+                if (j < np) load(S[j], j);
+            for (int k0 = 0; k0 < np; k0 += kBuf) {
+#pragma unroll
+                for (int j = 0; j < kBuf; ++j) {
+                    const int k = k0 + j;
+                    if (k < np) {
+                        process(S[j], k);
+                        if (k + kBuf < np) load(S[j], k + kBuf);
+                    }
+                }
+            }
         }
-        float *rq = rec + q * (kD + 2);
-        rq[dv] = acc;
-        if (dv == 0) {
-            rq[kD] = M;
-            rq[kD + 1] = lsum;
+        if (bad_page && lane == 0 && p.dev_err) atomicOr(p.dev_err, 1);
+
+        // row sums over the 4 lane groups that share a query row
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+
+        // merge the 4 waves through LDS into record w + (b H_kv + g)
+        __syncthreads();
+        float *ow = (float *)lds;  // [4 waves][16 rows][128 dv]
+#pragma unroll
+        for (int dc = 0; dc < 8; ++dc)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ow[(wave * 16 + n) * kD + 16 * dc + 4 * grp + r] = o[dc][r];
+        if (grp == 0) {
+            red_m[wave][n] = m;
+            red_l[wave][n] = l;
         }
+        __syncthreads();
+        float *rec = p.rec + ((int64_t)w + (int64_t)b * p.H_kv + g) * p.qrows * (kD + 2);
+        for (int idx = tid; idx < p.qrows * kD; idx += 256) {
+            const int q = idx / kD, dv = idx % kD;
+            float M = fmaxf(fmaxf(red_m[0][q], red_m[1][q]), fmaxf(red_m[2][q], red_m[3][q]));
+            float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float mw = red_m[i][q];
+                const float f = (mw == -INFINITY) ? 0.0f : exp2_fast(mw - M);
+                acc += ow[(i * 16 + q) * kD + dv] * f;
+                lsum += red_l[i][q] * f;
+            }
+            float *rq = rec + q * (kD + 2);
+            rq[dv] = acc;
+            if (dv == 0) {
+                rq[kD] = M;
+                rq[kD + 1] = lsum;
+            }
+        }
+
+        // next unit with pages, if the range goes on
+        pos = ubase + p1;
+        if (pos >= end) break;
+        ubase += c;
+        if (++g == p.H_kv) {
+            g = 0;
+            do {
+                ++b;
+                c = seq_pages(p, b);
+            } while (c == 0 && b + 1 < p.B);
+            if (c == 0) break;  // unreachable: pos < end <= T leaves pages to take
+        }
+        __syncthreads();  // the merge buffers are reused
     }
 }
 
@@ -246,17 +358,24 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
     const int L = p.ctx_len[b];
     __bf16 *op = p.out + b * p.so[0] + h * p.so[1];
     if (L < 1 || L > p.max_pages * kPage) {
+        if (h == 0 && dv == 0 && p.dev_err) atomicOr(p.dev_err, 2);
         op[dv] = (__bf16)0.0f;
         return;
     }
-    const int npages = (L + kPage - 1) / kPage;
-    const int ns = (npages + p.split_pages - 1) / p.split_pages;
-    const float *base = p.ws + ((int64_t)b * p.H_kv + g) * p.num_splits * p.qrows * (kD + 2);
+    // the work-groups whose ranges covered unit (b, g): those holding its first
+    // and last page and every one between (work-group w holds page x iff
+    // w T / W <= x < (w + 1) T / W, so w = floor(((x + 1) W - 1) / T))
+    const int excl = p.pref[b], c = p.pref[b + 1] - excl;
+    const int64_t T = (int64_t)p.pref[p.B] * p.H_kv, W = active_wgs(p, T);
+    const int64_t ubase = (int64_t)excl * p.H_kv + (int64_t)g * c;
+    const int64_t w0 = ((ubase + 1) * W - 1) / T, w1 = ((ubase + c) * W - 1) / T;
+    const int ns = (int)(w1 - w0 + 1);
+    const float *base = p.rec + (w0 + (int64_t)b * p.H_kv + g) * p.qrows * (kD + 2);
     float ob[2];
 #pragma unroll
     for (int br = 0; br < 2; ++br) {
         const int q = 2 * j + br;
-        // the splits' loads are independent: unrolled so they are in flight together
+        // the records' loads are independent: unrolled so they are in flight together
         float M = -INFINITY;
 #pragma unroll 8
         for (int s = 0; s < ns; ++s) M = fmaxf(M, base[((int64_t)s * p.qrows + q) * (kD + 2) + kD]);
@@ -286,6 +405,26 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
     op[dv] = (__bf16)y;
 }
 
+// Work-groups of the split pass that fit on the device at once; cached per
+// device (compute-unit count times the kernel's occupancy per unit).
+int resident_split_wgs() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel, 256, 0) != hipSuccess)
+        return 1;
+    const int r = std::max(1, cus * per_cu);
+    if (dev >= 0 && dev < kMaxDevices) cache[dev].store(r, std::memory_order_relaxed);
+    return r;
+}
+
 }  // namespace
 
 hipError_t launch_decode_bf16(const diffattn_decode_args &a, const DecodePlan &plan, void *workspace,
@@ -305,21 +444,24 @@ hipError_t launch_decode_bf16(const diffattn_decode_args &a, const DecodePlan &p
     p.lambda = a.lambda;
     p.gamma = a.gamma;
     p.out = (__bf16 *)a.out;
-    p.ws = (float *)workspace;
+    p.pref = (int32_t *)workspace;
+    p.rec = (float *)((unsigned char *)workspace + plan.header_bytes);
     p.dev_err = a.dev_err;
+    p.B = a.B;
     p.H = a.H;
     p.H_kv = a.H_kv;
     p.group = a.H / a.H_kv;
     p.qrows = plan.qrows;
     p.max_pages = a.max_pages;
     p.num_pages = a.num_pages;
-    p.split_pages = plan.split_pages;
-    p.num_splits = plan.num_splits;
+    p.target = plan.target_pages;
+    p.num_wgs = plan.target_pages > 0 ? plan.max_wgs
+                                      : std::min(plan.max_wgs, kRounds * resident_split_wgs());
     p.norm = a.norm == DIFFATTN_NORM_RMS;
     p.sc_log2 = scale * kLog2e;
     p.eps = a.eps;
     p.one_minus_init = 1.0f - lambda_init;
-    hipLaunchKernelGGL(decode_split_kernel, dim3(plan.num_splits, a.H_kv, a.B), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(decode_split_kernel, dim3(p.num_wgs), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(a.H, a.B), dim3(128), 0, stream, p);

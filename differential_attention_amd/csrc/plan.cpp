@@ -185,8 +185,12 @@ int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::str
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: scale must be finite and >= 0");
     if (a->norm == DIFFATTN_NORM_RMS && !(a->eps > 0.0f && !isinf(a->eps)))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: eps must be finite and > 0");
-    if (a->split_pages < 0 || a->split_pages > 64)
-        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: split_pages must be in [0, 64]");
+    if (a->split_pages < 0 || a->split_pages > kDecodeMaxTarget)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: split_pages must be in [0, 2^24]");
+    if ((int64_t)a->B * a->max_pages > INT32_MAX)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: B * max_pages must fit in 31 bits");
+    if ((int64_t)a->B * a->H_kv * a->max_pages > ((int64_t)1 << 40))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: B * H_kv * max_pages must be <= 2^40");
     if ((int64_t)a->max_pages * a->page_size > (1 << 30))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: max_pages * page_size too large");
     if (a->dtype != DIFFATTN_BF16 || a->d_qk != 128 || a->d_v != 128 || a->page_size != 64)
@@ -198,21 +202,18 @@ int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::str
     if (a->k1_cache != a->k2_cache)
         return fail(msg, DIFFATTN_EUNSUPPORTED, "diffattn_decode: the branches must share the key cache");
 
-    // plan: enough (sequence, KV head, split) items to fill the chip several times over
-    const int64_t units = (int64_t)(a->B > 0 ? a->B : 1) * a->H_kv;
-    int sp = a->split_pages;
-    if (sp == 0) {
-        int64_t want = (8192 + units - 1) / units;
-        want = std::max<int64_t>(1, std::min<int64_t>(want, a->max_pages));
-        sp = (int)((a->max_pages + want - 1) / want);
-        sp = std::max(sp, 8);  // at least 512 tokens per item
-    }
-    sp = std::min(std::min(sp, a->max_pages), 64);  // a split's page ids fit one wave
-    plan->split_pages = sp;
-    plan->num_splits = (a->max_pages + sp - 1) / sp;
+    // plan: the split pass has at most max_wgs work-groups; the records hold one
+    // partial state per (work-group, unit) pair, of which there are fewer than
+    // work-groups + units (consecutive ranges share at most one unit)
+    const int64_t units = (int64_t)a->B * a->H_kv;
+    const int64_t most_pages = units * a->max_pages;
+    const int64_t per_wg = a->split_pages > 0 ? a->split_pages : kDecodeMinPages;
+    plan->target_pages = a->split_pages;
+    plan->max_wgs = (int)std::max<int64_t>(1, std::min<int64_t>(kDecodeMaxWgs, (most_pages + per_wg - 1) / per_wg));
     plan->qrows = 2 * group;
-    plan->ws_bytes = (size_t)(a->B > 0 ? a->B : 0) * a->H_kv * plan->num_splits * plan->qrows *
-                     (size_t)(a->d_v + 2) * sizeof(float);
+    plan->header_bytes = ((size_t)(a->B + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    plan->record_bytes = (size_t)plan->qrows * (a->d_v + 2) * sizeof(float);
+    plan->ws_bytes = a->B > 0 ? plan->header_bytes + (size_t)(plan->max_wgs + units) * plan->record_bytes : 0;
 
     return DIFFATTN_OK;
 }

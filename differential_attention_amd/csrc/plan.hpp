@@ -11,15 +11,25 @@
 
 namespace da {
 
-// Split-KV decode plan: the pages of each sequence are cut into splits of
-// split_pages pages; every (sequence, KV head, split) is one work item whose
-// partial softmax state (max, sum, unnormalised output per query row) goes to
-// the workspace, and a second pass merges the splits.
+// Split-KV decode plan. The work is the list of (sequence, KV head) units in
+// order, each holding its sequence's pages; the split pass cuts this global
+// page list into equal contiguous ranges, one per work-group, so every
+// work-group streams the same number of pages whatever the length mix. A
+// range may end inside a unit and may span several; each (work-group, unit)
+// pair it touches yields one partial softmax state (max, sum, unnormalised
+// output per query row) in the workspace, and a second pass merges the
+// partial states of each unit.
+constexpr int kDecodeMaxWgs = 2048;   // work-groups of the split pass, at most
+constexpr int kDecodeMinPages = 4;    // pages per work-group, at least (library's choice)
+constexpr int kDecodeMaxTarget = 1 << 24;
+
 struct DecodePlan {
-    int split_pages = 0;  // pages per split
-    int num_splits = 0;   // splits per sequence (for the longest possible sequence)
-    int qrows = 0;        // query rows per KV head = 2 * (H / H_kv)
-    size_t ws_bytes = 0;  // workspace bytes
+    int target_pages = 0;      // pages per work-group asked for; 0 = library's choice
+    int max_wgs = 0;           // work-groups the workspace is sized for
+    int qrows = 0;             // query rows per KV head = 2 * (H / H_kv)
+    size_t header_bytes = 0;   // int32 page prefix [B + 1], rounded up to 256 bytes
+    size_t record_bytes = 0;   // one partial state: qrows * (d_v + 2) floats
+    size_t ws_bytes = 0;       // workspace bytes: header + (max_wgs + B * H_kv) records
 };
 
 // Prefill kernel selection.

@@ -27,8 +27,9 @@
  *    every output untouched. diffattn_last_error() then describes it.
  *  - DIFFATTN_EHIP means a launch was attempted and the HIP runtime reported
  *    an error (for example, no device); outputs are then undefined.
- *  - The library holds no state between calls and is safe to call from
- *    several host threads (the last-error message is thread-local).
+ *  - The library holds no state between calls apart from a per-device
+ *    cache of the compute-unit count and kernel occupancy, and is safe to
+ *    call from several host threads (the last-error message is thread-local).
  */
 #ifndef DIFFATTN_H
 #define DIFFATTN_H
@@ -96,7 +97,10 @@ typedef struct {
  *   out         [B, H, d_v]                   strides so[0], so[1]
  * Supported: dtype DIFFATTN_BF16, d_qk == d_v == 128, page_size 64,
  * H / H_kv <= 8 query heads per KV head in each branch.
- * split_pages: pages per split-KV work item, 0..64 (0 = chosen by the library).
+ * split_pages: pages per work-group of the split-KV pass, 0..2^24. The pages
+ * of all (sequence, KV head) pairs are cut into equal contiguous ranges, one
+ * per work-group (at most 2048); 0 lets the library use one round of the
+ * work-groups the device holds at once (at least 4 pages each).
  * dev_err: optional device int; bit 0 is OR-ed in when a page id outside
  * [0, num_pages) is met, bit 1 when a ctx_len is out of range. Such pages or
  * sequences are skipped (never read). NULL disables the report (the checks
@@ -142,9 +146,10 @@ int diffattn_lambda(const float *lq1, const float *lk1, const float *lq2, const 
 int diffattn_prefill(const diffattn_prefill_args *a, void *stream);
 
 /*
- * Bytes of device workspace diffattn_decode needs for these arguments
- * (split-KV partial results). Only sizes and flags are examined (pointers
- * may be NULL). Returns 0 if they are invalid.
+ * Bytes of device workspace diffattn_decode needs for these arguments: the
+ * page prefix over the sequences and the split-KV partial results (one per
+ * (work-group, sequence and KV head) pair). Only sizes and flags are examined
+ * (pointers may be NULL). Returns 0 if they are invalid or B == 0.
  */
 size_t diffattn_decode_workspace_bytes(const diffattn_decode_args *a);
 

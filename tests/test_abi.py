@@ -162,15 +162,18 @@ def _decode_args(**kw):
 
 
 def test_decode_workspace_and_plan(lib):
-    a = _decode_args()
-    ws = lib.diffattn_decode_workspace_bytes(ctypes.byref(a))
-    # 64 sequences x 8 KV heads x splits x 8 query rows x (128 + 2) floats
-    per_split = 64 * 8 * 8 * 130 * 4
-    assert ws > 0 and ws % per_split == 0
-    splits = ws // per_split
-    assert 2 <= splits <= 512
-    a = _decode_args(split_pages=64)
-    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == 8 * per_split
+    # header: int32 page prefix [B + 1] rounded up to 256 bytes; records: one
+    # per (work-group, unit) pair, fewer than work-groups + units, each
+    # 2 * (H / H_kv) query rows x (128 + 2) floats
+    header = -(-65 * 4 // 256) * 256
+    record = 4 * 2 * 130 * 4  # H / H_kv = 4
+    units = 64 * 8
+    a = _decode_args()  # library's choice: at most 2048 work-groups
+    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == header + (2048 + units) * record
+    a = _decode_args(split_pages=1024)  # 64 * 8 * 512 pages / 1024 = 256 work-groups
+    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == header + (256 + units) * record
+    a = _decode_args(B=1, H=2, H_kv=1, max_pages=3)  # 3 pages: 1 work-group of at least 4 pages
+    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == 256 + (1 + 1) * 4 * 130 * 4
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -181,6 +184,7 @@ def test_decode_workspace_and_plan(lib):
     ("k2_cache", FAKE + 5 * (1 << 34), da.EUNSUPPORTED),
     ("page_table", None, da.EINVAL),
     ("split_pages", -1, da.EINVAL),
+    ("split_pages", (1 << 24) + 1, da.EINVAL),
     ("out", FAKE, da.EINVAL),           # overlaps q1
 ])
 def test_decode_rejects(lib, field, value, code):

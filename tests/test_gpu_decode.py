@@ -71,11 +71,30 @@ def small(B=6, lens=None, H=8, H_kv=2, seed=0, max_pages=16):
 
 
 @pytest.mark.parametrize("lens", [[1, 63, 64, 65, 128, 1000], [1024, 777, 5, 129]])
-@pytest.mark.parametrize("split_pages", [0, 1, 3])
+@pytest.mark.parametrize("split_pages", [0, 1, 3, 7, 1 << 20])
 def test_decode_ragged(torch, da, lens, split_pages):
     c = DecodeCase(small(lens=lens), torch, da)
     say(f"decode lens {lens} split_pages {split_pages}")
     check(c.run(split_pages=split_pages).float().cpu().numpy(), c.oracle(), "bf16", "decode")
+
+
+@pytest.mark.parametrize("split_pages", [0, 50, 1 << 20])
+def test_decode_long_ranges(torch, da, split_pages):
+    # sequences of more than 64 pages: a work-group's range spans page-id
+    # chunks and, with few work-groups, several whole sequences
+    lens = [5000, 300, 9000, 4480]
+    c = DecodeCase(small(lens=lens, H=4, H_kv=2, seed=11, max_pages=160), torch, da)
+    say(f"decode long lens {lens} split_pages {split_pages}")
+    check(c.run(split_pages=split_pages).float().cpu().numpy(), c.oracle(), "bf16", "decode long")
+
+
+def test_decode_all_lengths_invalid(torch, da):
+    d = small(lens=[64, 100], seed=12)
+    d.ctx_len[:] = [0, 16 * 64 + 1]
+    c = DecodeCase(d, torch, da)
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    out = c.run(dev_err=err).float().cpu().numpy()
+    assert err.item() == 2 and np.all(out == 0)
 
 
 @pytest.mark.parametrize("H,H_kv", [(8, 8), (16, 2), (4, 4), (6, 2)])
