@@ -131,9 +131,14 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     constexpr int KC = DQK / 16;           // 16-wide k steps of the QK contraction
     constexpr int NBR = S::kNBr;           // branches computed by one wave
     constexpr int NW = S::kThreads / 64;   // waves per work-group
-    // with split branches the epilogue reuses the stages for 4 waves x 64 lanes x 64 floats
-    constexpr int kLdsBytes = (S::kOn && 2 * T::kStage < 65536) ? 65536 : 2 * T::kStage;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
+    // Two stages in two distinct LDS objects: the compiler then knows that the
+    // reads of one stage do not depend on the asynchronous copies into the
+    // other, and does not wait for the next tile's loads before reading this
+    // one. With split branches the epilogue reuses the stages for 4 waves x
+    // 64 lanes x 64 floats (two row groups in each).
+    constexpr int kStageBytes = (S::kOn && T::kStage < 32768) ? 32768 : T::kStage;
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[kStageBytes];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -201,9 +206,8 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     // hold the K tile(s), the rest the V tile. Slot -> (row, physical chunk)
     // -> logical chunk through the row's swizzle.
     static_assert(T::kBlocks % NW == 0, "stage blocks must divide among the waves");
-    auto issue_tile = [&](int t, int stage) {
+    auto issue_tile = [&](int t, unsigned char *base) {
         const int key0 = t * kBN;
-        unsigned char *base = lds + stage * T::kStage;
 #pragma unroll
         for (int i = 0; i < T::kBlocks / NW; ++i) {
             const int blk = wave + NW * i;
@@ -333,13 +337,8 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         }
     };
 
-    // ---- the key sweep
-    if (ntiles > 0) issue_tile(0, 0);
-    for (int t = 0; t < ntiles; ++t) {
-        wait_vmem_all();
-        __syncthreads();  // tile t visible to all waves; tile t-1 no longer read
-        if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
-        const unsigned char *base = lds + (t & 1) * T::kStage;
+    // ---- the key sweep: even tiles in stage 0, odd tiles in stage 1
+    auto tile_body = [&](const unsigned char *base, int t) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int j = 2 * t + sb;
@@ -352,6 +351,18 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
                 step(base, sb, true, lim);
             }
         }
+    };
+    if (ntiles > 0) issue_tile(0, st0);
+    for (int t = 0; t < ntiles; t += 2) {
+        wait_vmem_all();
+        __syncthreads();  // tile t visible to all waves; tile t-1 no longer read
+        if (t + 1 < ntiles) issue_tile(t + 1, st1);
+        tile_body(st0, t);
+        if (t + 1 >= ntiles) break;
+        wait_vmem_all();
+        __syncthreads();  // tile t+1 visible to all waves; tile t no longer read
+        if (t + 2 < ntiles) issue_tile(t + 2, st0);
+        tile_body(st1, t + 1);
     }
 
     // ---- epilogue: y = O1 / l1 - lambda O2 / l2 (then the V1 norm), bf16 store
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     if constexpr (S::kOn) {
         // branch-2 waves hand lambda O2 / l2 to their branch-1 partner through LDS
         __syncthreads();  // every wave is done with the key tiles
-        float *xch = (float *)lds + ((rg * 64 + lane) * 64);  // this lane's 64 values
+        float *xch = (float *)(rg < 2 ? st0 : st1) + (((rg & 1) * 64 + lane) * 64);  // this lane's 64 values
         if (br0) {
             const float r2 = p.lambda[h] / l[0];
 #pragma unroll
