@@ -49,12 +49,17 @@ def prefill_flops(B, H, N, dqk, dv):
 
 
 def decode_bytes(d):
+    """Algorithmic HBM bytes of one decode call: every visible token's keys
+    (one cache, or one per branch) and values once, the queries, the output,
+    the page-table entries used and ctx_len (plus gamma for the V1 norm)."""
     L = d.ctx_len.astype(np.int64)
-    kv = int(L.sum()) * d.H_kv * (d.d_qk + d.d_v) * 2
+    nk = 1 if d.shared_k else 2
+    kv = int(L.sum()) * d.H_kv * (nk * d.d_qk + d.d_v) * 2
     q = d.B * 2 * d.H * d.d_qk * 2
     out = d.B * d.H * d.d_v * 2
     table = int(((L + d.page - 1) // d.page).sum()) * 4 + d.B * 4
-    return kv + q + out + table
+    gamma = d.H * d.d_v * 4 if d.norm else 0
+    return kv + q + out + table + gamma
 
 
 # sources of the kernels each workload runs (their hash keys the stored counters)
@@ -63,6 +68,7 @@ KERNEL_SOURCES = {
     "prefill_v2": ["prefill_bf16.hip", "common.hpp"],
     "longctx_v1": ["prefill_bf16.hip", "common.hpp"],
     "decode_v2": ["decode.hip", "common.hpp"],
+    "decode_v1": ["decode.hip", "common.hpp"],
 }
 
 
@@ -132,19 +138,29 @@ def single_workload(args, torch, da, W, dev):
         call = lambda: dst.copy_(src)
         work, unit, metric, bound = 2.0 * n * 2, "GB/s", "device copy GB/s (read + write)", "hbm"
         desc = "torch copy_ of 2^31 bf16 elements (4 GiB read, 4 GiB written)"
-    elif name == "decode_v2":
-        d = W.decode_v2()
-        qd = to_dev(d.q_full)
+    elif name in ("decode_v2", "decode_v1"):
+        d = getattr(W, name)()
+        if d.q_full is not None:
+            qd = to_dev(d.q_full)
+            q1, q2 = qd[:, 0::2], qd[:, 1::2]
+        else:
+            q1, q2 = to_dev(d.q1), to_dev(d.q2)
         kc, vc = to_dev(d.k1_cache), to_dev(d.v_cache)
+        kc2 = None if d.shared_k else to_dev(d.k2_cache)
         table, ctx = torch.from_numpy(d.page_table).to(dev), torch.from_numpy(d.ctx_len).to(dev)
         lam = da.lambda_(*(torch.from_numpy(x).to(dev) for x in (d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2)), d.depth)
+        gamma = torch.from_numpy(d.gamma).to(dev) if d.norm else None
         out = torch.empty((d.B, d.H, d.d_v), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(da.decode_workspace_bytes(qd[:, 0::2], qd[:, 1::2], kc, vc, table, ctx, lam,
-                                                   depth=d.depth), dtype=torch.uint8, device=dev)
-        call = lambda: da.decode(qd[:, 0::2], qd[:, 1::2], kc, vc, table, ctx, lam, depth=d.depth, out=out,
-                                 workspace=ws)
+        kw = dict(depth=d.depth, norm=d.norm, gamma=gamma, eps=d.eps, k2_cache=kc2)
+        ws = torch.empty(da.decode_workspace_bytes(q1, q2, kc, vc, table, ctx, lam, **kw),
+                         dtype=torch.uint8, device=dev)
+        call = lambda: da.decode(q1, q2, kc, vc, table, ctx, lam, out=out, workspace=ws, **kw)
         work, unit, metric, bound = decode_bytes(d), "GB/s", "decode GB/s (algorithmic HBM bytes)", "hbm"
-        desc = "decode_v2: V2 paged decode, 64 seqs, ctx U{8192..32768}, 8 KV / 64 Q heads, d 128, page 64"
+        if name == "decode_v2":
+            desc = "decode_v2: V2 paged decode, 64 seqs, ctx U{8192..32768}, 8 KV / 64 Q heads, d 128, page 64"
+        else:
+            desc = ("decode_v1: V1 paged decode, 64 seqs, ctx U{8192..32768}, 8 KV / 32 heads, d_qk 64 "
+                    "(K1, K2 caches), d_v 128, page 64, RMS norm")
     else:
         p = getattr(W, name)()
         dt = p.dtype
@@ -197,7 +213,8 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profiling aid: run only one part of the step")
     ap.add_argument("--workload", default="step",
-                    choices=["step", "prefill_v1", "prefill_v2", "longctx_v1", "tiny_v1", "decode_v2", "copy"],
+                    choices=["step", "prefill_v1", "prefill_v2", "longctx_v1", "tiny_v1", "decode_v2",
+                             "decode_v1", "copy"],
                     help="step: the whole path (default); otherwise time one workload alone "
                          "(copy: a plain device copy of 4 GiB, for calibrating HBM byte counters)")
     args = ap.parse_args()

@@ -217,7 +217,8 @@ def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm
         raise ValueError("q1/q2 need unit innermost stride")
     a.sq1 = _c_int64_2(q1.stride(0), q1.stride(1))
     a.sq2 = _c_int64_2(q2.stride(0), q2.stride(1))
-    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()
+            and (k2_cache is None or k2_cache.is_contiguous())):
         raise ValueError("caches must be contiguous")
     a.k1_cache = _ptr(k_cache)
     a.k2_cache = _ptr(k2_cache if k2_cache is not None else k_cache)
@@ -241,27 +242,29 @@ def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm
 
 def decode_workspace_bytes(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int,
                            norm: bool = False, gamma=None, eps: float = 1e-5, scale: float = 0.0,
-                           split_pages: int = 0) -> int:
+                           split_pages: int = 0, k2_cache=None) -> int:
     a = _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
-                     scale, None, split_pages, None)
+                     scale, None, split_pages, None, k2_cache)
     return int(load_library().diffattn_decode_workspace_bytes(ctypes.byref(a)))
 
 
 def decode(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int, norm: bool = False,
            gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, workspace=None,
-           split_pages: int = 0, dev_err=None, stream=None):
+           split_pages: int = 0, dev_err=None, stream=None, k2_cache=None):
     """Paged decode (one query token per sequence).
 
-    q1, q2 [B, H, d]; k_cache, v_cache [num_pages, H_kv, page, d] contiguous
-    (one key cache serves both branches); page_table [B, max_pages] int32;
-    ctx_len [B] int32; lam [H] fp32. Returns out [B, H, d_v]."""
+    q1, q2 [B, H, d_qk]; k_cache [num_pages, H_kv, page, d_qk] and v_cache
+    [num_pages, H_kv, page, d_v] contiguous; k_cache serves both branches
+    unless k2_cache (the branch-2 keys, V1 form with d_qk 64) is given;
+    page_table [B, max_pages] int32; ctx_len [B] int32; lam [H] fp32.
+    Returns out [B, H, d_v]."""
     import torch
     B, H, _ = q1.shape
     dv = v_cache.shape[3]
     if out is None:
         out = torch.empty((B, H, dv), dtype=q1.dtype, device=q1.device)
     a = _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
-                     scale, out, split_pages, dev_err)
+                     scale, out, split_pages, dev_err, k2_cache)
     lib = load_library()
     need = int(lib.diffattn_decode_workspace_bytes(ctypes.byref(a)))
     if workspace is None:

@@ -1,7 +1,10 @@
-// decode.hip -- split-KV paged decode of differential attention, V2 form
-// (lesson "Differential Attention V2", section "V1 vs V2": the query heads
-// are doubled, the KV heads stay, so the KV cache is loaded once per step and
-// every key/value byte feeds all query heads of its group, both branches).
+// decode.hip -- split-KV paged decode of differential attention
+// (lesson "Differential Attention V2", section "V1 vs V2"). V2 form: the
+// query heads are doubled, the KV heads stay, so the KV cache is loaded once
+// per step and every key/value byte feeds all query heads of its group, both
+// branches. V1 form (d_qk 64, separate K1 and K2 caches, value width 128):
+// the value cache that a two-call implementation reads once per branch is
+// read once here for both, and the combine applies the V1 norm.
 //
 // Work decomposition. The (sequence, KV head) units, in order, with their
 // pages form one global page list of T pages. Pass 1 (decode_split_kernel)
@@ -20,7 +23,8 @@
 //
 // Inside a range, all 2 * group query rows of the KV head (both branches of
 // every pair) form one 16-column MFMA operand, so each K and V byte is read
-// from HBM exactly once. Each of the 4 waves owns a 16-token slice of every
+// from HBM exactly once (V1: the K1 product with the branch-2 columns zeroed
+// plus the K2 product with the branch-1 columns zeroed fill one accumulator). Each of the 4 waves owns a 16-token slice of every
 // page and streams it independently -- no barrier inside the page loop: the
 // next kBuf pages' K and V slices are loaded into registers while the current
 // one is used, so every wave keeps HBM requests in flight.
@@ -56,7 +60,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kD = 128;      // d_qk = d_v
+constexpr int kDV = 128;     // value width (and the width of a record row)
 constexpr int kPage = 64;    // tokens per page
 #ifndef DIFFATTN_DECODE_KBUF
 #define DIFFATTN_DECODE_KBUF 2
@@ -70,13 +74,13 @@ constexpr int kRounds = DIFFATTN_DECODE_ROUNDS;  // rounds of resident work-grou
 struct DecodeParams {
     const __bf16 *q1, *q2;
     int64_t sq1[2], sq2[2];
-    const __bf16 *kc, *vc;
+    const __bf16 *kc, *kc2, *vc;  // kc2: the branch-2 key cache (d_qk 64; == kc for d_qk 128)
     const int32_t *page_table, *ctx_len;
     const float *lambda, *gamma;
     __bf16 *out;
     int64_t so[2];
     int32_t *pref;  // workspace header: pages of the valid sequences before b, [B + 1]
-    float *rec;     // workspace records, qrows * (kD + 2) floats each
+    float *rec;     // workspace records, qrows * (kDV + 2) floats each
     int *dev_err;
     int B, H, H_kv, group, qrows, max_pages, num_pages, target, num_wgs, norm;
     float sc_log2, eps, one_minus_init;
@@ -127,13 +131,14 @@ __device__ __forceinline__ int block_scan(int x, int *sh, int *total) {
 
 // one wave's 16-token slice of a page: K operands and V rows
 struct Slice {
-    uint4 k[4];  // k[kc]: token 16 w + lane % 16, features 32 kc + 8 (lane / 16) .. +7
+    uint4 k[4];  // k[kc]: token 16 w + lane % 16, 8 features from 8 (lane / 16) (see the Q fragments)
     uint4 v[4];  // v[i]: token 16 w + 4 i + lane / 16, features 8 (lane % 16) .. +7
     bool ok;     // the page id was valid
 };
 
+template <int DQK>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * 16 * kD * 4];  // 32 KB
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * 16 * kDV * 4];  // 32 KB
     __shared__ float red_m[4][16], red_l[4][16];
     __shared__ int sh[4], s_b, s_excl;
 
@@ -188,7 +193,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         const int p1 = (int)(min(end, ubase + c) - ubase);
         const int L = p.ctx_len[b];
 
-        // Q^T fragments: lane supplies query row n, d = 32 kc + 8 grp .. +7
+        // Q^T fragments: lane supplies query row n (pair n / 2, branch n % 2).
+        // d_qk 128: k step kc covers features 32 kc + 8 grp .. +7 of the shared
+        // keys. d_qk 64: k steps 0, 1 contract K1 with the branch-1 rows and
+        // steps 2, 3 contract K2 with the branch-2 rows (each with the other
+        // branch's rows zero), so one accumulator gets each row's own scores.
         bf16x8 qf[4];
         {
             const bool ok = n < p.qrows;
@@ -198,7 +207,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
                 uint4 z = {0u, 0u, 0u, 0u};
-                qf[kc] = as_bf16x8(ok ? ldg16(q + 32 * kc + 8 * grp) : z);
+                const bool use = DQK == 128 ? ok : (ok && br == (kc >> 1));
+                qf[kc] = as_bf16x8(use ? ldg16(q + 32 * (DQK == 128 ? kc : (kc & 1)) + 8 * grp) : z);
             }
         }
 
@@ -220,13 +230,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 S.ok = phys >= 0 && phys < p.num_pages;
                 bad_page |= !S.ok;
                 phys = S.ok ? phys : 0;
-                const int64_t base = (((int64_t)phys * p.H_kv + g) * kPage + 16 * wave) * kD;
-                const __bf16 *kp = p.kc + base + n * kD + 8 * grp;
-                const __bf16 *vp = p.vc + base + grp * kD + 8 * n;
+                const int64_t row0 = ((int64_t)phys * p.H_kv + g) * kPage + 16 * wave;  // first token row
+                const __bf16 *vp = p.vc + row0 * kDV + grp * kDV + 8 * n;
+                if (DQK == 128) {
+                    const __bf16 *kp = p.kc + (row0 + n) * DQK + 8 * grp;
 #pragma unroll
-                for (int kc = 0; kc < 4; ++kc) S.k[kc] = ldg16(kp + 32 * kc);
+                    for (int kc = 0; kc < 4; ++kc) S.k[kc] = ldg16(kp + 32 * kc);
+                } else {
+                    const __bf16 *kp1 = p.kc + (row0 + n) * DQK + 8 * grp;
+                    const __bf16 *kp2 = p.kc2 + (row0 + n) * DQK + 8 * grp;
+                    S.k[0] = ldg16(kp1);
+                    S.k[1] = ldg16(kp1 + 32);
+                    S.k[2] = ldg16(kp2);
+                    S.k[3] = ldg16(kp2 + 32);
+                }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S.v[i] = ldg16(vp + 4 * i * kD);
+                for (int i = 0; i < 4; ++i) S.v[i] = ldg16(vp + 4 * i * kDV);
             };
 
             auto process = [&](const Slice &S, int k) {
@@ -309,29 +328,29 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
         for (int dc = 0; dc < 8; ++dc)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ow[(wave * 16 + n) * kD + 16 * dc + 4 * grp + r] = o[dc][r];
+            for (int r = 0; r < 4; ++r) ow[(wave * 16 + n) * kDV + 16 * dc + 4 * grp + r] = o[dc][r];
         if (grp == 0) {
             red_m[wave][n] = m;
             red_l[wave][n] = l;
         }
         __syncthreads();
-        float *rec = p.rec + ((int64_t)w + (int64_t)b * p.H_kv + g) * p.qrows * (kD + 2);
-        for (int idx = tid; idx < p.qrows * kD; idx += 256) {
-            const int q = idx / kD, dv = idx % kD;
+        float *rec = p.rec + ((int64_t)w + (int64_t)b * p.H_kv + g) * p.qrows * (kDV + 2);
+        for (int idx = tid; idx < p.qrows * kDV; idx += 256) {
+            const int q = idx / kDV, dv = idx % kDV;
             float M = fmaxf(fmaxf(red_m[0][q], red_m[1][q]), fmaxf(red_m[2][q], red_m[3][q]));
             float acc = 0.0f, lsum = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float mw = red_m[i][q];
                 const float f = (mw == -INFINITY) ? 0.0f : exp2_fast(mw - M);
-                acc += ow[(i * 16 + q) * kD + dv] * f;
+                acc += ow[(i * 16 + q) * kDV + dv] * f;
                 lsum += red_l[i][q] * f;
             }
-            float *rq = rec + q * (kD + 2);
+            float *rq = rec + q * (kDV + 2);
             rq[dv] = acc;
             if (dv == 0) {
-                rq[kD] = M;
-                rq[kD + 1] = lsum;
+                rq[kDV] = M;
+                rq[kDV + 1] = lsum;
             }
         }
 
@@ -370,7 +389,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
     const int64_t ubase = (int64_t)excl * p.H_kv + (int64_t)g * c;
     const int64_t w0 = ((ubase + 1) * W - 1) / T, w1 = ((ubase + c) * W - 1) / T;
     const int ns = (int)(w1 - w0 + 1);
-    const float *base = p.rec + (w0 + (int64_t)b * p.H_kv + g) * p.qrows * (kD + 2);
+    const float *base = p.rec + (w0 + (int64_t)b * p.H_kv + g) * p.qrows * (kDV + 2);
     float ob[2];
 #pragma unroll
     for (int br = 0; br < 2; ++br) {
@@ -378,15 +397,15 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
         // the records' loads are independent: unrolled so they are in flight together
         float M = -INFINITY;
 #pragma unroll 8
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, base[((int64_t)s * p.qrows + q) * (kD + 2) + kD]);
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, base[((int64_t)s * p.qrows + q) * (kDV + 2) + kDV]);
         float acc = 0.0f, lsum = 0.0f;
 #pragma unroll 8
         for (int s = 0; s < ns; ++s) {
-            const float *rq = base + ((int64_t)s * p.qrows + q) * (kD + 2);
-            const float ms = rq[kD];
+            const float *rq = base + ((int64_t)s * p.qrows + q) * (kDV + 2);
+            const float ms = rq[kDV];
             const float f = (ms == -INFINITY) ? 0.0f : exp2_fast(ms - M);
             acc += rq[dv] * f;
-            lsum += rq[kD + 1] * f;
+            lsum += rq[kDV + 1] * f;
         }
         ob[br] = lsum > 0.0f ? acc / lsum : 0.0f;
     }
@@ -400,13 +419,14 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
         if ((dv & 63) == 0) red[dv >> 6] = ss;
         __syncthreads();
         ss = red[0] + red[1];
-        y *= p.one_minus_init / sqrtf(ss * (1.0f / kD) + p.eps) * p.gamma[(int64_t)h * kD + dv];
+        y *= p.one_minus_init / sqrtf(ss * (1.0f / kDV) + p.eps) * p.gamma[(int64_t)h * kDV + dv];
     }
     op[dv] = (__bf16)y;
 }
 
 // Work-groups of the split pass that fit on the device at once; cached per
 // device (compute-unit count times the kernel's occupancy per unit).
+template <int DQK>
 int resident_split_wgs() {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cache[kMaxDevices];
@@ -418,7 +438,7 @@ int resident_split_wgs() {
     }
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel, 256, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<DQK>, 256, 0) != hipSuccess)
         return 1;
     const int r = std::max(1, cus * per_cu);
     if (dev >= 0 && dev < kMaxDevices) cache[dev].store(r, std::memory_order_relaxed);
@@ -438,6 +458,7 @@ hipError_t launch_decode_bf16(const diffattn_decode_args &a, const DecodePlan &p
         p.so[k] = a.so[k];
     }
     p.kc = (const __bf16 *)a.k1_cache;
+    p.kc2 = (const __bf16 *)a.k2_cache;
     p.vc = (const __bf16 *)a.v_cache;
     p.page_table = a.page_table;
     p.ctx_len = a.ctx_len;
@@ -455,13 +476,18 @@ hipError_t launch_decode_bf16(const diffattn_decode_args &a, const DecodePlan &p
     p.max_pages = a.max_pages;
     p.num_pages = a.num_pages;
     p.target = plan.target_pages;
-    p.num_wgs = plan.target_pages > 0 ? plan.max_wgs
-                                      : std::min(plan.max_wgs, kRounds * resident_split_wgs());
+    const bool d64 = a.d_qk == 64;
+    p.num_wgs = plan.target_pages > 0
+                    ? plan.max_wgs
+                    : std::min(plan.max_wgs, kRounds * (d64 ? resident_split_wgs<64>() : resident_split_wgs<128>()));
     p.norm = a.norm == DIFFATTN_NORM_RMS;
     p.sc_log2 = scale * kLog2e;
     p.eps = a.eps;
     p.one_minus_init = 1.0f - lambda_init;
-    hipLaunchKernelGGL(decode_split_kernel, dim3(p.num_wgs), dim3(256), 0, stream, p);
+    if (d64)
+        hipLaunchKernelGGL(decode_split_kernel<64>, dim3(p.num_wgs), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(decode_split_kernel<128>, dim3(p.num_wgs), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(a.H, a.B), dim3(128), 0, stream, p);

@@ -193,14 +193,15 @@ int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::str
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: B * H_kv * max_pages must be <= 2^40");
     if ((int64_t)a->max_pages * a->page_size > (1 << 30))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: max_pages * page_size too large");
-    if (a->dtype != DIFFATTN_BF16 || a->d_qk != 128 || a->d_v != 128 || a->page_size != 64)
+    if (a->dtype != DIFFATTN_BF16 || (a->d_qk != 128 && a->d_qk != 64) || a->d_v != 128 || a->page_size != 64)
         return fail(msg, DIFFATTN_EUNSUPPORTED,
-                    "diffattn_decode: supports bf16 with d_qk = d_v = 128 and page_size 64");
+                    "diffattn_decode: supports bf16 with d_qk in {64, 128}, d_v = 128 and page_size 64");
     const int group = a->H / a->H_kv;
     if (group > 8)
         return fail(msg, DIFFATTN_EUNSUPPORTED, "diffattn_decode: at most 8 output heads per KV head");
-    if (a->k1_cache != a->k2_cache)
-        return fail(msg, DIFFATTN_EUNSUPPORTED, "diffattn_decode: the branches must share the key cache");
+    if (a->d_qk == 128 && a->k1_cache != a->k2_cache)
+        return fail(msg, DIFFATTN_EUNSUPPORTED,
+                    "diffattn_decode: with d_qk = 128 the branches must share the key cache");
 
     // plan: the split pass has at most max_wgs work-groups; the records hold one
     // partial state per (work-group, unit) pair, of which there are fewer than
@@ -221,7 +222,7 @@ int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::str
 int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *msg) {
     int rc = check_decode_sizes(a, plan, msg);
     if (rc != DIFFATTN_OK || a->B == 0) return rc;
-    if (!a->q1 || !a->q2 || !a->k1_cache || !a->v_cache || !a->page_table || !a->ctx_len ||
+    if (!a->q1 || !a->q2 || !a->k1_cache || !a->k2_cache || !a->v_cache || !a->page_table || !a->ctx_len ||
         !a->lambda || !a->out)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: null pointer");
     if (a->norm == DIFFATTN_NORM_RMS && !a->gamma)
@@ -230,7 +231,7 @@ int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *m
     for (int64_t s : strides)
         if (s < 0 || s % 8 != 0)
             return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: strides must be non-negative multiples of 8");
-    const void *al16[] = {a->q1, a->q2, a->k1_cache, a->v_cache, a->out};
+    const void *al16[] = {a->q1, a->q2, a->k1_cache, a->k2_cache, a->v_cache, a->out};
     for (const void *p : al16)
         if (!aligned(p, 16)) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: tensor not 16-byte aligned");
     if (!aligned(a->page_table, 4) || !aligned(a->ctx_len, 4) || !aligned(a->lambda, 4))
@@ -244,6 +245,7 @@ int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *m
         const void *p;
         size_t bytes;
     } rs[] = {{a->k1_cache, (size_t)kv_elems * a->d_qk * 2},
+              {a->k2_cache, (size_t)kv_elems * a->d_qk * 2},
               {a->v_cache, (size_t)kv_elems * a->d_v * 2},
               {a->page_table, (size_t)a->B * a->max_pages * 4},
               {a->ctx_len, (size_t)a->B * 4},

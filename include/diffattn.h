@@ -90,13 +90,16 @@ typedef struct {
  * page_table[b * max_pages + t / page_size], slot t % page_size.
  *   q1, q2      [B, H, d_qk]                  strides sq*[0] (b), sq*[1] (h)
  *   k1_cache,
- *   k2_cache    [num_pages, H_kv, page_size, d_qk] contiguous; k1 == k2 (V2)
- *   v_cache     [num_pages, H_kv, page_size, d_v]  contiguous
+ *   k2_cache    [num_pages, H_kv, page_size, d_qk] contiguous; one cache for
+ *               both branches (V2, k1 == k2) or one per branch (V1)
+ *   v_cache     [num_pages, H_kv, page_size, d_v]  contiguous, read once for
+ *               both branches
  *   page_table  [B, max_pages] int32 device
  *   ctx_len     [B] int32 device, 1 <= ctx_len[b] <= max_pages * page_size
  *   out         [B, H, d_v]                   strides so[0], so[1]
- * Supported: dtype DIFFATTN_BF16, d_qk == d_v == 128, page_size 64,
- * H / H_kv <= 8 query heads per KV head in each branch.
+ * Supported: dtype DIFFATTN_BF16, d_v 128, page_size 64, H / H_kv <= 8
+ * output heads per KV head, and d_qk 128 with k1_cache == k2_cache (V2) or
+ * d_qk 64 with any two key caches (V1).
  * split_pages: pages per work-group of the split-KV pass, 0..2^24. The pages
  * of all (sequence, KV head) pairs are cut into equal contiguous ranges, one
  * per work-group (at most 2048); 0 lets the library use one round of the

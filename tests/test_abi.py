@@ -172,12 +172,14 @@ def test_decode_workspace_and_plan(lib):
     assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == header + (2048 + units) * record
     a = _decode_args(split_pages=1024)  # 64 * 8 * 512 pages / 1024 = 256 work-groups
     assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == header + (256 + units) * record
+    a = _decode_args(d_qk=64, k2_cache=FAKE + 5 * (1 << 34))  # V1 form: same records
+    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == header + (2048 + units) * record
     a = _decode_args(B=1, H=2, H_kv=1, max_pages=3)  # 3 pages: 1 work-group of at least 4 pages
     assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == 256 + (1 + 1) * 4 * 130 * 4
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("d_qk", 64, da.EUNSUPPORTED),
+    ("d_qk", 96, da.EUNSUPPORTED),
     ("page_size", 32, da.EUNSUPPORTED),
     ("dtype", da.F32, da.EUNSUPPORTED),
     ("H", 36, da.EINVAL),               # not a multiple of H_kv

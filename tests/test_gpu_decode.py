@@ -26,20 +26,24 @@ def da():
 class DecodeCase:
     def __init__(self, d: W.Decode, torch, da):
         self.d, self.torch, self.da = d, torch, da
-        qf = to_dev(d.q_full, "bf16")
-        self.q1, self.q2 = qf[:, 0::2], qf[:, 1::2]
+        if d.q_full is not None:
+            qf = to_dev(d.q_full, "bf16")
+            self.q1, self.q2 = qf[:, 0::2], qf[:, 1::2]
+        else:
+            self.q1, self.q2 = to_dev(d.q1, "bf16"), to_dev(d.q2, "bf16")
         self.kc = to_dev(d.k1_cache, "bf16")
+        self.kc2 = None if d.shared_k else to_dev(d.k2_cache, "bf16")
         self.vc = to_dev(d.v_cache, "bf16")
         self.table = torch.from_numpy(d.page_table).to(dev())
         self.ctx = torch.from_numpy(d.ctx_len).to(dev())
         self.lam64 = oracle.lambda_(d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2, d.depth)
         vecs = [torch.from_numpy(x).to(dev()) for x in (d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2)]
         self.lam = da.lambda_(*vecs, d.depth)
-        self.gamma = None
+        self.gamma = torch.from_numpy(d.gamma).to(dev()) if d.norm else None
 
     def run(self, **kw):
         d = self.d
-        args = dict(depth=d.depth, norm=d.norm, gamma=self.gamma, eps=d.eps)
+        args = dict(depth=d.depth, norm=d.norm, gamma=self.gamma, eps=d.eps, k2_cache=self.kc2)
         args.update(kw)
         return self.da.decode(self.q1, self.q2, self.kc, self.vc, self.table, self.ctx, self.lam, **args)
 
@@ -47,9 +51,11 @@ class DecodeCase:
         """Oracle on all sequences, or on a subset with their pages compacted."""
         d = self.d
         norm = d.norm if norm is None else norm
+        if gamma is None and norm:
+            gamma = d.gamma
         if seqs is None:
-            kc = d.f32("k1_cache")
-            return oracle.decode(d.f32("q1"), d.f32("q2"), kc, kc, d.f32("v_cache"), d.page_table,
+            kc, kc2 = d.f32("k1_cache"), d.f32("k2_cache")
+            return oracle.decode(d.f32("q1"), d.f32("q2"), kc, kc2, d.f32("v_cache"), d.page_table,
                                  d.ctx_len, self.lam64, depth=d.depth, norm=norm, gamma=gamma)
         seqs = np.asarray(seqs)
         npg = (d.ctx_len[seqs] + d.page - 1) // d.page
@@ -59,8 +65,9 @@ class DecodeCase:
         for r, (b, n) in enumerate(zip(seqs, npg)):
             table[r, :n] = [remap[int(p)] for p in d.page_table[b, :n]]
         kc = W.bf16_to_f32(d.k1_cache[used])
+        kc2 = W.bf16_to_f32(d.k2_cache[used])
         vc = W.bf16_to_f32(d.v_cache[used])
-        return oracle.decode(d.f32("q1")[seqs], d.f32("q2")[seqs], kc, kc, vc, table, d.ctx_len[seqs],
+        return oracle.decode(d.f32("q1")[seqs], d.f32("q2")[seqs], kc, kc2, vc, table, d.ctx_len[seqs],
                              self.lam64, depth=d.depth, norm=norm, gamma=gamma)
 
 
@@ -178,3 +185,71 @@ def test_decode_v2_full(torch, da):
     out = c.run().float().cpu().numpy()
     seqs = np.array([0, 7, int(np.argmax(d.ctx_len)), int(np.argmin(d.ctx_len)), 33, 63])
     check(out[seqs], c.oracle(seqs=seqs), "bf16", "decode_v2 sampled sequences")
+
+
+# ---- V1 form: d_qk 64, separate K1 and K2 caches, value width 128, RMS norm
+
+
+def small_v1(lens, H=8, H_kv=2, seed=0, max_pages=16):
+    return W.decode_v1(seed=seed, B=len(lens), H=H, H_kv=H_kv, max_pages=max_pages,
+                       ctx_len=np.array(lens))
+
+
+@pytest.mark.parametrize("lens", [[1, 63, 64, 65, 128, 1000], [1024, 777, 5, 129]])
+@pytest.mark.parametrize("split_pages", [0, 1, 3, 1 << 20])
+def test_decode_v1_ragged(torch, da, lens, split_pages):
+    c = DecodeCase(small_v1(lens, seed=21), torch, da)
+    say(f"decode V1 lens {lens} split_pages {split_pages}")
+    check(c.run(split_pages=split_pages).float().cpu().numpy(), c.oracle(), "bf16", "decode V1")
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 8), (16, 2), (6, 2)])
+def test_decode_v1_groupings(torch, da, H, H_kv):
+    c = DecodeCase(small_v1([300, 64, 1, 700, 129], H=H, H_kv=H_kv, seed=22 + H), torch, da)
+    say(f"decode V1 H {H} H_kv {H_kv}")
+    check(c.run().float().cpu().numpy(), c.oracle(), "bf16", "decode V1 grouping")
+
+
+def test_decode_v1_no_norm_and_swapped_caches(torch, da):
+    # without the norm the V1 result is O1 - lambda O2; swapping (Q1, K1) with
+    # (Q2, K2) must use each branch's own key cache, checked against the oracle
+    d = small_v1([200, 500, 64], seed=23)
+    c = DecodeCase(d, torch, da)
+    check(c.run(norm=False).float().cpu().numpy(), c.oracle(norm=False), "bf16", "decode V1 no norm")
+    c.q1, c.q2, c.kc, c.kc2 = c.q2, c.q1, c.kc2, c.kc
+    d.q1, d.q2, d.k1_cache, d.k2_cache = d.q2, d.q1, d.k2_cache, d.k1_cache
+    check(c.run(norm=False).float().cpu().numpy(), c.oracle(norm=False), "bf16", "decode V1 swapped")
+
+
+def test_decode_v1_matches_prefill_last_row(torch, da):
+    # one V1 sequence stored in pages in order equals the last row of a causal
+    # V1 prefill (with the norm) over the same tokens
+    L, H, H_kv = 333, 4, 4
+    d = small_v1([L], H=H, H_kv=H_kv, seed=24)
+    c = DecodeCase(d, torch, da)
+    dec = c.run().float()
+    npg = (L + 63) // 64
+    pages = d.page_table[0, :npg]
+
+    def gather(cache, width):
+        return cache[pages].transpose(1, 0, 2, 3).reshape(H_kv, npg * 64, width)[:, :L][None]
+
+    k1, k2, v = gather(d.k1_cache, 64), gather(d.k2_cache, 64), gather(d.v_cache, 128)
+    q1 = np.zeros((1, H, L, 64), np.uint16)
+    q2 = np.zeros((1, H, L, 64), np.uint16)
+    q1[0, :, L - 1] = d.q1[0]
+    q2[0, :, L - 1] = d.q2[0]
+    pre = da.prefill(to_dev(q1, "bf16"), to_dev(q2, "bf16"), to_dev(k1, "bf16"), to_dev(k2, "bf16"),
+                     to_dev(v, "bf16"), c.lam, depth=d.depth, causal=True, norm=True, gamma=c.gamma,
+                     eps=d.eps)
+    diff = (pre[0, :, L - 1].float() - dec[0]).abs().max().item()
+    assert diff <= 1.6e-2, diff
+
+
+def test_decode_v1_full(torch, da):
+    d = W.decode_v1()
+    say(f"decode_v1 full: 64 sequences, {d.num_pages} pages, context {d.ctx_len.min()}..{d.ctx_len.max()}")
+    c = DecodeCase(d, torch, da)
+    out = c.run().float().cpu().numpy()
+    seqs = np.array([0, 5, int(np.argmax(d.ctx_len)), int(np.argmin(d.ctx_len)), 40, 63])
+    check(out[seqs], c.oracle(seqs=seqs), "bf16", "decode_v1 sampled sequences")

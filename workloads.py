@@ -21,6 +21,9 @@ d_head 128 shape, and its exercise on GQA with 8 KV heads and 32 query heads):
                    causal, bf16, d 128, depth 20.
 * ``decode_v2``    V2 paged decode, 64 sequences, context U{8192..32768},
                    page 64, 8 KV heads, 64 query heads, bf16, d 128, depth 20.
+* ``decode_v1``    V1 paged decode, the same sequences and pages as the V2
+                   decode's shape family with d_qk 64 (separate K1, K2 caches),
+                   d_v 128, 32 heads over 8 KV heads, RMS norm, depth 12.
 * ``longctx_v1``   V1, B 1, H 8, N 65536, causal, bf16, d_qk 64, d_v 128,
                    16 planted signal keys per head (the lesson's signal-plus-
                    noise toy, section "Build it, step 4", at 64K scale).
@@ -257,6 +260,53 @@ def decode_v2(seed: int = 4, B: int = 64, H: int = 32, H_kv: int = 8, d: int = 1
     return Decode("decode_v2", "bf16", B, H, H_kv, d, d, page, max_pages, P,
                   q[:, 0::2], q[:, 1::2], k_cache, k_cache, v_cache, table, ctx_len,
                   lq1, lk1, lq2, lk2, depth=depth, norm=False, gamma=None, q_full=q)
+
+
+def decode_v1(seed: int = 6, B: int = 64, H: int = 32, H_kv: int = 8, d_qk: int = 64,
+              d_v: int = 128, page: int = 64, max_pages: int = 512, ctx_lo: int = 8192,
+              ctx_hi: int = 32768, depth: int = 12, ctx_len: Optional[np.ndarray] = None) -> Decode:
+    """V1 paged decode, bf16: the V2 decode's shape family with the V1 head
+    split (d_qk 64 per branch, separate K1 and K2 caches, one V cache of width
+    128) and the V1 norm. Draw order: ctx_len ~ U{ctx_lo..ctx_hi}; a random
+    permutation of the P = sum ceil(L_b/page) physical pages assigned to
+    (sequence, logical page) in order (unused table slots -1); K1, K2 pools
+    [P, H_kv, page, d_qk] and the V pool [P, H_kv, page, d_v], each
+    0.5 N(0,1) (slots past a sequence's length are random and must be masked);
+    Q1, Q2 [B, H, d_qk] ~ 0.5 N(0,1); lambda vectors [H, d_qk] ~ N(0, 0.1^2);
+    gamma [H, d_v] ~ U(0.9, 1.1); depth 12; RMS norm."""
+    rng = np.random.default_rng(seed)
+    if ctx_len is None:
+        ctx_len = rng.integers(ctx_lo, ctx_hi + 1, size=B).astype(np.int32)
+    else:
+        ctx_len = np.asarray(ctx_len, np.int32)
+        assert ctx_len.shape == (B,)
+    npg = (ctx_len.astype(np.int64) + page - 1) // page
+    assert int(npg.max()) <= max_pages
+    P = int(npg.sum())
+    perm = rng.permutation(P).astype(np.int32)
+    table = np.full((B, max_pages), -1, np.int32)
+    pos = 0
+    for b in range(B):
+        n = int(npg[b])
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+
+    def pool(d):
+        out = np.empty((P, H_kv, page, d), np.uint16)
+        chunk = max(1, (1 << 24) // (H_kv * page * d))
+        for s in range(0, P, chunk):
+            e = min(P, s + chunk)
+            out[s:e] = f32_to_bf16(_normal(rng, (e - s, H_kv, page, d), 0.5))
+        return out
+
+    k1_cache, k2_cache, v_cache = pool(d_qk), pool(d_qk), pool(d_v)
+    q1 = f32_to_bf16(_normal(rng, (B, H, d_qk), 0.5))
+    q2 = f32_to_bf16(_normal(rng, (B, H, d_qk), 0.5))
+    lq1, lk1, lq2, lk2 = _lambda_vectors(rng, H, d_qk)
+    gamma = rng.uniform(0.9, 1.1, size=(H, d_v)).astype(np.float32)
+    return Decode("decode_v1", "bf16", B, H, H_kv, d_qk, d_v, page, max_pages, P,
+                  q1, q2, k1_cache, k2_cache, v_cache, table, ctx_len,
+                  lq1, lk1, lq2, lk2, depth=depth, norm=True, gamma=gamma, shared_k=False)
 
 
 def longctx_v1(seed: int = 5, B: int = 1, H: int = 8, N: int = 65536, d_qk: int = 64,
