@@ -46,8 +46,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
-        build()
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()  # missing, or older than its source (its signatures may have changed)
     lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     i, d, i64 = ctypes.c_int, ctypes.c_double, ctypes.c_int64
@@ -55,7 +55,7 @@ def _load():
     lib.oracle_lambda_init.restype = d
     lib.oracle_lambda.argtypes = [P, P, P, P, i, i, i, P]
     lib.oracle_lambda.restype = None
-    lib.oracle_prefill.argtypes = [P, P, P, P, P, i, i, i, i, i, i, P, i, i, d, i, P, d, P, i64, P]
+    lib.oracle_prefill.argtypes = [P, P, P, P, P, i, i, i, i, i, i, P, i, i, i, d, i, P, d, P, i64, P]
     lib.oracle_prefill.restype = i
     lib.oracle_decode.argtypes = [P, P, P, P, P, i, i, i, i, i, i, i, i, P, P, P, i, d, i, P, d, P]
     lib.oracle_decode.restype = i
@@ -93,11 +93,12 @@ def lambda_(lq1, lk1, lq2, lk2, depth: int) -> np.ndarray:
 
 def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool, norm: bool,
             gamma=None, eps: float = 1e-5, scale: Optional[float] = None,
-            rows: Optional[np.ndarray] = None) -> np.ndarray:
+            rows: Optional[np.ndarray] = None, window: int = 0) -> np.ndarray:
     """Differential attention over a full sequence.
 
     q1, q2 [B, H, N, d_qk]; k1, k2 [B, H_kv, N, d_qk]; v [B, H_kv, N, d_v];
-    lam [H]. Returns [B, H, N, d_v] fp64, or [len(rows), d_v] when ``rows``
+    lam [H]; window: 0, or a causal sliding window W (keys i-W+1..i).
+    Returns [B, H, N, d_v] fp64, or [len(rows), d_v] when ``rows``
     (flat ids (b*H + h)*N + i) is given."""
     q1, q2, k1, k2, v = (_f32(x) for x in (q1, q2, k1, k2, v))
     B, H, N, dqk = q1.shape
@@ -119,7 +120,8 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool, norm: bool,
         out = np.empty((nrows, dv), np.float64)
         rp = _ptr(rows)
     rc = _load().oracle_prefill(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), B, H, Hkv, N, dqk, dv,
-                                _ptr(lam), int(depth), int(bool(causal)), float(scale), int(bool(norm)),
+                                _ptr(lam), int(depth), int(bool(causal)), int(window), float(scale),
+                                int(bool(norm)),
                                 _ptr(g), float(eps), rp, nrows, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_prefill: invalid argument")

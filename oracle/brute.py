@@ -19,12 +19,13 @@ from typing import List, Optional, Sequence
 Matrix = List[List[float]]
 
 
-def _scores(Q: Matrix, K: Matrix, scale: float, causal: bool) -> Matrix:
+def _scores(Q: Matrix, K: Matrix, scale: float, causal: bool, window: int = 0) -> Matrix:
     n_q, n_k = len(Q), len(K)
     S = [[0.0] * n_k for _ in range(n_q)]
     for i in range(n_q):
         for j in range(n_k):
-            if causal and j > i:
+            # causal: j <= i; a sliding window W also needs j >= i - W + 1
+            if (causal and j > i) or (window > 0 and j < i - window + 1):
                 S[i][j] = -math.inf
             else:
                 S[i][j] = math.fsum(a * b for a, b in zip(Q[i], K[j])) * scale
@@ -44,13 +45,14 @@ def _softmax_rows(S: Matrix) -> Matrix:
 def diff_attention(Q1: Matrix, K1: Matrix, Q2: Matrix, K2: Matrix, V: Matrix, lam: float,
                    *, causal: bool, scale: Optional[float] = None, norm: bool = False,
                    gamma: Optional[Sequence[float]] = None, eps: float = 1e-5,
-                   lambda_init: float = 0.0) -> Matrix:
-    """One head. Q*, K* are [n, d_qk] lists; V is [n, d_v]. Returns [n, d_v]."""
+                   lambda_init: float = 0.0, window: int = 0) -> Matrix:
+    """One head. Q*, K* are [n, d_qk] lists; V is [n, d_v]. Returns [n, d_v].
+    window > 0 (with causal) keeps keys i - window + 1 .. i of row i."""
     d = len(Q1[0])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    A1 = _softmax_rows(_scores(Q1, K1, scale, causal))
-    A2 = _softmax_rows(_scores(Q2, K2, scale, causal))
+    A1 = _softmax_rows(_scores(Q1, K1, scale, causal, window))
+    A2 = _softmax_rows(_scores(Q2, K2, scale, causal, window))
     W = [[a - lam * b for a, b in zip(r1, r2)] for r1, r2 in zip(A1, A2)]
     d_v = len(V[0])
     out = []

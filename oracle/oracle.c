@@ -20,7 +20,10 @@
  *        difference; V2 drops it and keeps the KV heads of GQA while doubling
  *        the query heads.
  *   [AV] lesson "Attention Variants" (phase 7 lesson 15), "Build it", step 1:
- *        the causal mask admits key j for query i iff j <= i.
+ *        the causal mask admits key j for query i iff j <= i; step 2 and the
+ *        sliding-window figure of its "Concept" section: a causal window of W
+ *        admits key j iff i - W + 1 <= j <= i (W keys, the query's own
+ *        included; W >= N is the full causal mask).
  *   [SK] the integrator skill page of the same lesson: the default depth
  *        schedule lambda_init = 0.8 - 0.6 exp(-0.3 (depth - 1)).
  *
@@ -136,6 +139,7 @@ static void diff_row(const float *q1, const float *q2,
  * Prefill. Layouts (row-major, contiguous):
  *   q1, q2 [B, H, N, d_qk]; k1, k2 [B, H_kv, N, d_qk]; v [B, H_kv, N, d_v];
  *   lambda [H]; gamma [H, d_v] (used when norm != 0).
+ * window: 0 for none, else the causal sliding window W (needs causal).
  * rows: flat row ids r = (b * H + h) * N + i to compute (NULL: all B*H*N rows,
  * in that order); out [nrows, d_v] fp64.
  * Returns 0, or -1 on an invalid argument.
@@ -143,11 +147,12 @@ static void diff_row(const float *q1, const float *q2,
 int oracle_prefill(const float *q1, const float *q2, const float *k1,
                    const float *k2, const float *v, int B, int H, int H_kv,
                    int N, int d_qk, int d_v, const double *lambda, int depth,
-                   int causal, double scale, int norm, const float *gamma,
+                   int causal, int window, double scale, int norm, const float *gamma,
                    double eps, const int64_t *rows, int64_t nrows, double *out)
 {
     if (B < 0 || H <= 0 || H_kv <= 0 || N < 0 || d_qk <= 0 || d_v <= 0) return -1;
     if (H % H_kv != 0) return -1;
+    if (window < 0 || (window > 0 && !causal)) return -1;
     if (norm && !gamma) return -1;
     int64_t total = (int64_t)B * H * N;
     if (!rows) nrows = total;
@@ -171,12 +176,15 @@ int oracle_prefill(const float *q1, const float *q2, const float *k1,
             int h = (int)(bh % H);
             int b = (int)(bh / H);
             int g = h / group;
-            int64_t n = causal ? i + 1 : N;      /* [AV] j <= i */
+            int64_t lo = 0, hi = N;                /* visible keys [lo, hi) */
+            if (causal) hi = i + 1;                /* [AV] j <= i */
+            if (window > 0 && i - window + 1 > 0) lo = i - window + 1; /* [AV] window */
+            int64_t n = hi - lo;
             int64_t kvbase = ((int64_t)b * H_kv + g) * N;
             for (int64_t j = 0; j < n; ++j) {
-                kp1[j] = k1 + (kvbase + j) * d_qk;
-                kp2[j] = k2 + (kvbase + j) * d_qk;
-                vp[j] = v + (kvbase + j) * d_v;
+                kp1[j] = k1 + (kvbase + lo + j) * d_qk;
+                kp2[j] = k2 + (kvbase + lo + j) * d_qk;
+                vp[j] = v + (kvbase + lo + j) * d_v;
             }
             diff_row(q1 + r * d_qk, q2 + r * d_qk, kp1, kp2, vp, n, d_qk, d_v,
                      lambda[h], scale, norm, norm ? gamma + (int64_t)h * d_v : NULL,

@@ -423,3 +423,87 @@ def test_toy_noise_cancels_signal_survives():
     grid = np.linspace(0.0, 1.0, 41)
     snrs = [snr(_toy_weights(q, k1, k2, lam)) for lam in grid]
     assert abs(grid[int(np.argmax(snrs))] - lam_star) <= 0.5 * (grid[1] - grid[0]) + 1e-12
+
+
+# --------------------------------------------------------------------------
+# causal sliding window (lesson "Attention Variants", "Build it", step 2 and
+# the sliding-window figure of its "Concept" section): row i sees keys
+# i - W + 1 .. i
+# --------------------------------------------------------------------------
+
+
+def test_swa_mask_matches_printed_figure():
+    fig = _read_mask("swa_mask_8_w4.txt")
+    N = fig.shape[0]
+    rng = np.random.default_rng(14)
+    q1, q2, k1, k2 = (rnd(rng, 1, 1, N, 4) for _ in range(4))
+    v = rnd(rng, 1, 1, N, 3)
+    base = _prefill(q1, q2, k1, k2, v, [0.3], causal=True, norm=False, window=4)
+    seen = np.zeros((N, N), bool)
+    for j in range(N):
+        kk, vv = k1.copy(), v.copy()
+        kk[0, 0, j] += 1.0
+        vv[0, 0, j] += 1.0
+        out = _prefill(q1, q2, kk, k2, vv, [0.3], causal=True, norm=False, window=4)
+        seen[:, j] = np.any(out[0, 0] != base[0, 0], axis=-1)
+    np.testing.assert_array_equal(seen, fig)
+
+
+def test_swa_window_at_least_n_is_full_causal_bitwise():
+    rng = np.random.default_rng(15)
+    N = 37
+    q1, q2, k1, k2 = (rnd(rng, 2, 3, N, 8) for _ in range(4))
+    v = rnd(rng, 2, 3, N, 5)
+    lam = [0.1, 0.5, 0.9]
+    g = rng.uniform(0.9, 1.1, (3, 5)).astype(np.float32)
+    full = _prefill(q1, q2, k1, k2, v, lam, causal=True, norm=True, gamma=g)
+    for w in (N, N + 1, 10 * N):
+        got = _prefill(q1, q2, k1, k2, v, lam, causal=True, norm=True, gamma=g, window=w)
+        assert np.array_equal(got, full)
+
+
+def test_swa_window_one_sees_only_itself():
+    # each row's only key is its own: both softmaxes are 1, y = (1 - lambda) v_i
+    rng = np.random.default_rng(16)
+    N = 20
+    q1, q2, k1, k2 = (rnd(rng, 1, 2, N, 6) for _ in range(4))
+    v = rnd(rng, 1, 2, N, 4)
+    lam = np.array([0.25, -0.5])
+    got = _prefill(q1, q2, k1, k2, v, lam, causal=True, norm=False, window=1)
+    ref = (1.0 - lam)[None, :, None, None] * v.astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("window", [1, 2, 3, 5, 9])
+def test_swa_matches_brute(window):
+    rng = np.random.default_rng(17 + window)
+    N, dqk, dv = 11, 4, 3
+    q1, q2, k1, k2 = (rnd(rng, 1, 1, N, dqk) for _ in range(4))
+    v = rnd(rng, 1, 1, N, dv)
+    got = _prefill(q1, q2, k1, k2, v, [0.7], causal=True, norm=False, window=window)
+    ref = brute.diff_attention(*(x[0, 0].astype(np.float64).tolist() for x in (q1, k1, q2, k2, v)), 0.7,
+                               causal=True, window=window)
+    np.testing.assert_allclose(got[0, 0], np.array(ref), rtol=1e-12, atol=1e-13)
+
+
+def test_swa_row_equals_causal_attention_over_its_window():
+    # row i with window W is the last row of a plain causal attention over the
+    # W keys i-W+1..i alone (a different construction: the sequence is cut)
+    rng = np.random.default_rng(18)
+    N, W = 40, 7
+    q1, q2, k1, k2 = (rnd(rng, 1, 2, N, 8) for _ in range(4))
+    v = rnd(rng, 1, 2, N, 6)
+    lam = [0.3, 0.8]
+    got = _prefill(q1, q2, k1, k2, v, lam, causal=True, norm=False, window=W)
+    for i in (0, 3, W - 1, W, 25, N - 1):
+        lo = max(0, i - W + 1)
+        cut = lambda x: np.ascontiguousarray(x[:, :, lo:i + 1])
+        sub = _prefill(cut(q1), cut(q2), cut(k1), cut(k2), cut(v), lam, causal=True, norm=False)
+        np.testing.assert_allclose(got[0, :, i], sub[0, :, -1], rtol=1e-13, atol=1e-14)
+
+
+def test_swa_needs_causal():
+    rng = np.random.default_rng(19)
+    x = rnd(rng, 1, 1, 4, 2)
+    with pytest.raises(ValueError):
+        _prefill(x, x, x, x, x, [0.1], causal=False, norm=False, window=2)
