@@ -50,6 +50,7 @@ class PrefillArgs(ctypes.Structure):
         ("eps", ctypes.c_float),
         ("out", ctypes.c_void_p),
         ("so", _c_int64_3),
+        ("window", ctypes.c_int),
     ]
 
 
@@ -167,13 +168,14 @@ def _strides3(t):
 
 
 def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool = True, norm: bool = False,
-            gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, stream=None):
+            gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, stream=None, window: int = 0):
     """Differential-attention prefill.
 
     q1, q2 [B, H, N, d_qk]; k1, k2 [B, H_kv, N, d_qk] (pass the same tensor
     for both in the V2 form); v [B, H_kv, N, d_v]; lam [H] fp32 device;
     gamma [H, d_v] fp32 device when norm (V1). Views with unit innermost
-    stride are accepted as they are. Returns out [B, H, N, d_v]."""
+    stride are accepted as they are. window > 0 (causal only) limits row i to
+    keys i-window+1 .. i. Returns out [B, H, N, d_v]."""
     import torch
     B, H, N, dqk = q1.shape
     Hkv, dv = k1.shape[1], v.shape[3]
@@ -194,6 +196,7 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool = True, norm: bo
     a.lambda_ = _ptr(lam)
     a.depth = int(depth)
     a.causal = int(bool(causal))
+    a.window = int(window)
     a.scale = float(scale)
     a.norm = NORM_RMS if norm else NORM_NONE
     a.gamma = _ptr(gamma) if norm else None

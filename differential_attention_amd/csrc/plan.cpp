@@ -97,6 +97,8 @@ int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string
     if (a->d_qk < 1 || a->d_v < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: d_qk and d_v must be >= 1");
     if (a->depth < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: depth must be >= 1");
     if (a->causal != 0 && a->causal != 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: causal must be 0 or 1");
+    if (a->window < 0 || (a->window > 0 && !a->causal))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: window must be 0, or > 0 with causal");
     if (a->norm != DIFFATTN_NORM_NONE && a->norm != DIFFATTN_NORM_RMS)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: unknown norm");
     if (!(a->scale >= 0.0f) || isinf(a->scale))

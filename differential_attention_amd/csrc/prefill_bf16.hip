@@ -54,6 +54,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <climits>
+
 namespace da {
 
 namespace {
@@ -82,7 +84,7 @@ struct Bf16Params {
     int64_t sq1[3], sq2[3], sk1[3], sk2[3], sv[3], so[3];
     const float *lambda, *gamma;
     __bf16 *out;
-    int B, H, H_kv, group, N, causal, row_blocks, xcd_units;
+    int B, H, H_kv, group, N, causal, window, row_blocks, xcd_units;
     float sc_log2;  // scale * log2(e)
     float eps, one_minus_init;
 };
@@ -124,7 +126,7 @@ struct Tile {
     static constexpr int kRowsPerKBlock = 1024 / (2 * DQK);
 };
 
-template <int DQK, bool SHARED_K, bool NORM>
+template <int DQK, bool SHARED_K, bool NORM, bool WIN>
 __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void prefill_bf16_kernel(Bf16Params p) {
     using T = Tile<DQK, SHARED_K>;
     using S = Split<DQK>;
@@ -197,7 +199,15 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 
     const int kend = p.causal ? min(p.N, q0 + kBM) : p.N;
     const int ntiles = (kend + kBN - 1) / kBN;
-    // sub-blocks this wave needs; the last one is the only masked one
+    // causal window W: row i sees keys i-W+1 .. i, so tiles below the work-
+    // group's first row's window are never loaded, sub-blocks below this
+    // wave's first row's window are skipped, and sub-blocks holding a key
+    // below its last row's window start are masked from below
+    const int win = WIN ? p.window : 0;  // (a separate instantiation when windowed)
+    const int tlo = WIN ? max(0, q0 - win + 1) / kBN : 0;
+    const int jlo = WIN ? max(0, wrow0 - win + 1) / 32 : 0;
+    const int jmask = WIN ? (max(0, wrow0 + kWM - win) + 31) / 32 : 0;  // sub-blocks < jmask: lower mask
+    // sub-blocks this wave needs; the last one is masked from above
     const int wend = p.causal ? min(p.N, wrow0 + kWM) : p.N;
     const int nsub = wrow0 < p.N ? (wend + 31) / 32 : 0;
 
@@ -262,7 +272,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 
     // one branch of one sub-block: scores, online softmax (reference max moved
     // lazily), bf16 probabilities for the two 16-key steps
-    auto softmax_branch = [&](const unsigned char *kt, const bf16x8 *q, int sb, bool mask, int lim, float &mr,
+    auto softmax_branch = [&](const unsigned char *kt, const bf16x8 *q, int sb, bool mask, int lim, int lo, float &mr,
                               float &lr, f32x16 *orr, bf16x8 &pb0, bf16x8 &pb1) {
         f32x16 s = f32x16{};
 #pragma unroll
@@ -270,7 +280,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         if (mask) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (key_of_reg(r) >= lim) s[r] = -INFINITY;
+                if (key_of_reg(r) >= lim || key_of_reg(r) < lo) s[r] = -INFINITY;
         }
         float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
@@ -304,13 +314,13 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         pb1 = bf16x8{pp[4][0], pp[4][1], pp[5][0], pp[5][1], pp[6][0], pp[6][1], pp[7][0], pp[7][1]};
     };
 
-    auto step = [&](const unsigned char *base, int sb, bool mask, int lim) {
+    auto step = [&](const unsigned char *base, int sb, bool mask, int lim, int lo) {
         const unsigned char *vt = base + T::kNK * T::kKBytes;
         bf16x8 pb[NBR][2];
 #pragma unroll
         for (int j = 0; j < NBR; ++j) {
             const unsigned char *kt = base + (SHARED_K ? 0 : (br0 + j) * T::kKBytes);
-            softmax_branch(kt, qf[j], sb, mask, lim, m[j], l[j], o[j], pb[j][0], pb[j][1]);
+            softmax_branch(kt, qf[j], sb, mask, lim, lo, m[j], l[j], o[j], pb[j][0], pb[j][1]);
         }
         // O^T += V^T P^T, one V read for every branch of the wave; the next
         // step's V operand is read while this step's products run
@@ -342,18 +352,22 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int j = 2 * t + sb;
-            if (j < nsub - 1) {
-                step(base, sb, false, 0);
-            } else if (j == nsub - 1) {
-                // diagonal / ragged-end sub-block: key index >= lim is masked
+            if (j < jlo || j >= nsub) continue;  // wholly outside every row's window / past the diagonal
+            if (j < nsub - 1 && j >= jmask) {
+                step(base, sb, false, 0, 0);
+            } else {
+                // diagonal / ragged-end sub-block (keys >= lim masked) and
+                // window-start sub-blocks (keys < lo masked), relative to key0
                 const int key0 = j * 32 + 8 * hh;
                 const int lim = (p.causal ? min(myrow + 1, p.N) : p.N) - key0;
-                step(base, sb, true, lim);
+                const int lo = WIN ? myrow - win + 1 - key0 : INT_MIN / 2;
+                step(base, sb, true, lim, lo);
             }
         }
     };
-    if (ntiles > 0) issue_tile(0, st0);
-    for (int t = 0; t < ntiles; t += 2) {
+    // tiles tlo, tlo+1, ... alternate between stage 0 and stage 1
+    if (tlo < ntiles) issue_tile(tlo, st0);
+    for (int t = tlo; t < ntiles; t += 2) {
         wait_vmem_all();
         __syncthreads();  // tile t visible to all waves; tile t-1 no longer read
         if (t + 1 < ntiles) issue_tile(t + 1, st1);
@@ -443,8 +457,12 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 
 template <int DQK, bool SHARED_K, bool NORM>
 hipError_t launch_t(const Bf16Params &p, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<DQK, SHARED_K, NORM>), dim3(blocks), dim3(Split<DQK>::kThreads), 0,
-                       stream, p);
+    if (p.window > 0)
+        hipLaunchKernelGGL((prefill_bf16_kernel<DQK, SHARED_K, NORM, true>), dim3(blocks),
+                           dim3(Split<DQK>::kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_bf16_kernel<DQK, SHARED_K, NORM, false>), dim3(blocks),
+                           dim3(Split<DQK>::kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -475,6 +493,7 @@ hipError_t launch_prefill_bf16(const diffattn_prefill_args &a, float scale, floa
     p.group = a.H / a.H_kv;
     p.N = a.N;
     p.causal = a.causal;
+    p.window = a.window;
     p.row_blocks = (a.N + kBM - 1) / kBM;
     const int kv_units = a.B * a.H_kv;
     p.xcd_units = (kv_units % 8 == 0) ? kv_units / 8 : 0;

@@ -6,7 +6,8 @@
 //          Attention V2", section "Concept")
 //   V1:  y <- y / sqrt(mean(y^2) + eps) * gamma[h] * (1 - lambda_init)
 // Visible keys: j <= i when causal (lesson "Attention Variants", "Build it",
-// step 1), else all N.
+// step 1), else all N; with a causal window W also j >= i - W + 1 (same
+// lesson, step 2).
 //
 // One wave per query row, fp32 throughout. The softmax is exact two-pass
 // per row (first the maxima of both branches, then exponentials, sums and
@@ -24,7 +25,7 @@ struct PrefillF32Params {
     int64_t sq1[3], sq2[3], sk1[3], sk2[3], sv[3], so[3];
     const float *lambda, *gamma;
     float *out;
-    int H, group, N, d_qk, d_v, causal, norm;
+    int H, group, N, d_qk, d_v, causal, window, norm;
     float scale, eps, one_minus_init;
 };
 
@@ -47,10 +48,11 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillF32Params p) {
     const float *k2 = p.k2 + b * p.sk2[0] + g * p.sk2[1];
     const float *v = p.v + b * p.sv[0] + g * p.sv[1];
     const int kend = p.causal ? i + 1 : p.N;
+    const int kbeg = p.window > 0 ? max(0, i - p.window + 1) : 0;
 
     // pass 1: row maxima of the scaled scores of both branches
     float m1 = -INFINITY, m2 = -INFINITY;
-    for (int j0 = 0; j0 < kend; j0 += 64) {
+    for (int j0 = kbeg; j0 < kend; j0 += 64) {
         const int j = j0 + lane;
         if (j < kend) {
             m1 = fmaxf(m1, dot_row(q1, k1 + (int64_t)j * p.sk1[2], p.d_qk) * p.scale);
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillF32Params p) {
     const int c0 = lane, c1 = lane + 64;
     float l1 = 0.0f, l2 = 0.0f;
     float o1a = 0.0f, o1b = 0.0f, o2a = 0.0f, o2b = 0.0f;
-    for (int j0 = 0; j0 < kend; j0 += 64) {
+    for (int j0 = kbeg; j0 < kend; j0 += 64) {
         const int j = j0 + lane;
         float e1 = 0.0f, e2 = 0.0f;
         if (j < kend) {
@@ -137,6 +139,7 @@ hipError_t launch_prefill_f32(const diffattn_prefill_args &a, float scale, float
     p.d_qk = a.d_qk;
     p.d_v = a.d_v;
     p.causal = a.causal;
+    p.window = a.window;
     p.norm = a.norm == DIFFATTN_NORM_RMS;
     p.scale = scale;
     p.eps = a.eps;

@@ -14,7 +14,10 @@
  *   V2: the query heads are doubled while the KV heads stay as in GQA; both
  *       queries of a pair read the same KV head; no norm.
  * Causal mask (lesson "Attention Variants", phase 7 lesson 15, "Build it",
- * step 1): key j is visible to query i iff j <= i.
+ * step 1): key j is visible to query i iff j <= i. Causal sliding window of
+ * W keys (same lesson, step 2 and the sliding-window figure of "Concept"):
+ * key j is visible iff i - W + 1 <= j <= i; W >= N is the full causal mask.
+ * Key tiles wholly outside every row's window are never loaded.
  *
  * Conventions shared by every entry point:
  *  - Every tensor pointer is DEVICE memory owned by the caller. The library
@@ -81,6 +84,7 @@ typedef struct {
     float eps;           /* RMSNorm epsilon, > 0 */
     void *out;
     int64_t so[3];
+    int window;          /* 0: none; W > 0 (causal only): row i sees keys i-W+1 .. i */
 } diffattn_prefill_args;
 
 /*

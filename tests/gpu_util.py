@@ -80,13 +80,14 @@ class PrefillCase:
         return self.da.prefill(self.q1, self.q2, self.k1, self.k2, self.v,
                                self.lam if lam is None else lam, **args)
 
-    def oracle(self, rows=None, lam64=None):
+    def oracle(self, rows=None, lam64=None, window: int = 0):
         p = self.p
         k1 = p.f32("k1")
         k2 = k1 if p.shared_k else p.f32("k2")
         return oracle.prefill(p.f32("q1"), p.f32("q2"), k1, k2, p.f32("v"),
                               self.lam64 if lam64 is None else lam64, depth=p.depth,
-                              causal=p.causal, norm=p.norm, gamma=p.gamma, eps=p.eps, rows=rows)
+                              causal=p.causal, norm=p.norm, gamma=p.gamma, eps=p.eps, rows=rows,
+                              window=window)
 
 
 def gather_rows(out, rows: np.ndarray, H: int, N: int) -> np.ndarray:

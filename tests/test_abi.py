@@ -110,11 +110,18 @@ def _rc(lib, a):
     ("q1", None, da.EINVAL),
     ("gamma", None, da.EINVAL),          # RMS without gamma
     ("k1", FAKE + 2 * (1 << 24) + 2, da.EINVAL),   # misaligned bf16 pointer
+    ("window", -1, da.EINVAL),
 ])
 def test_prefill_rejects(lib, field, value, code):
     a = _prefill_args(**{field: value})
     assert _rc(lib, a) == code
     assert lib.diffattn_last_error().decode().startswith("diffattn_prefill")
+
+
+def test_prefill_window_needs_causal(lib):
+    a = _prefill_args(causal=0, window=16)
+    assert _rc(lib, a) == da.EINVAL
+    assert "window" in lib.diffattn_last_error().decode()
 
 
 def test_prefill_rejects_bad_strides_and_alias(lib):

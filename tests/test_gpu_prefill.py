@@ -181,3 +181,51 @@ def test_longctx_v1_full(torch, da):
     probe_rows = lambda b, h: np.unique(np.concatenate([p.probes[b, h, :, 0], p.probes[b, h, :, 1]]))
     rows = sampled_rows(p.B, p.H, p.N, seed=23, n_rand=16, edge=8, extra=probe_rows)
     check(gather_rows(out, rows, p.H, p.N), c.oracle(rows=rows), "bf16", "longctx_v1 sampled + probe rows")
+
+
+# ---------------------------------------------------------------- causal sliding window
+
+@pytest.mark.parametrize("form", ["v1", "v2"])
+@pytest.mark.parametrize("N,window", [(200, 1), (200, 17), (333, 32), (333, 33), (513, 64), (513, 100),
+                                      (513, 129), (700, 300)])
+def test_bf16_sliding_window(torch, da, form, N, window):
+    p = _bf16_case(form, N, True, seed=N + window)
+    c = PrefillCase(p)
+    say(f"bf16 {form} N {N} window {window}")
+    check(c.run(window=window).float().cpu().numpy(), c.oracle(window=window), "bf16",
+          f"{form} N={N} W={window}")
+
+
+@pytest.mark.parametrize("form", ["v1", "v2"])
+def test_bf16_window_at_least_n_is_full_causal_bitwise(torch, da, form):
+    p = _bf16_case(form, 333, True, seed=5)
+    c = PrefillCase(p)
+    full = c.run().clone()
+    for w in (333, 334, 5000):
+        assert torch.equal(c.run(window=w), full), w
+
+
+@pytest.mark.parametrize("N,window", [(1, 1), (77, 5), (130, 64), (130, 200)])
+def test_fp32_sliding_window(torch, da, N, window):
+    p = W.tiny_v1(seed=N, N=N, H=2)
+    c = PrefillCase(p)
+    say(f"f32 N {N} window {window}")
+    check(c.run(window=window).cpu().numpy(), c.oracle(window=window), "f32", f"f32 W={window}")
+
+
+def test_window_needs_causal(torch, da):
+    p = _bf16_case("v1", 64, False, B=1, seed=1)
+    c = PrefillCase(p)
+    with pytest.raises(RuntimeError):
+        c.run(window=8)
+
+
+def test_bf16_long_sequence_small_window_sampled(torch, da):
+    # V2 GQA at N 16384 with a 1024-key window (the 5:1 local-layer setting the
+    # lesson cites): key tiles outside the windows are skipped; rows sampled
+    p = W.prefill_v2(seed=31, N=16384)
+    c = PrefillCase(p)
+    say("prefill_v2 shape, window 1024, sampled rows")
+    out = c.run(window=1024)
+    rows = sampled_rows(p.B, p.H, p.N, seed=31, n_rand=24, edge=8)
+    check(gather_rows(out, rows, p.H, p.N), c.oracle(rows=rows, window=1024), "bf16", "v2 W=1024")
