@@ -44,8 +44,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def prefill_flops(B, H, N, dqk, dv):
-    return B * H * (N * N / 2.0) * 2.0 * (2 * dqk + 2 * dv)
+def prefill_flops(B, H, N, dqk, dv, window=0):
+    """Both branches, QK and PV, per visible (query, key) pair; causal pairs
+    counted as N^2/2, and with a causal window W < N as W^2/2 + (N - W) W."""
+    pairs = N * N / 2.0 if not window or window >= N else window * window / 2.0 + (N - window) * window
+    return B * H * pairs * 2.0 * (2 * dqk + 2 * dv)
 
 
 def decode_bytes(d):
@@ -175,11 +178,14 @@ def single_workload(args, torch, da, W, dev):
         gamma = torch.from_numpy(p.gamma).to(dev) if p.norm else None
         lam = da.lambda_(*(torch.from_numpy(x).to(dev) for x in (p.lam_q1, p.lam_k1, p.lam_q2, p.lam_k2)), p.depth)
         out = torch.empty((p.B, p.H, p.N, p.d_v), dtype=q1.dtype, device=dev)
+        win = args.window
         call = lambda: da.prefill(q1, q2, k1, k2, v, lam, depth=p.depth, causal=p.causal, norm=p.norm,
-                                  gamma=gamma, eps=p.eps, out=out)
-        work = prefill_flops(p.B, p.H, p.N, p.d_qk, p.d_v)
+                                  gamma=gamma, eps=p.eps, out=out, window=win)
+        work = prefill_flops(p.B, p.H, p.N, p.d_qk, p.d_v, win)
         unit, metric, bound = "TFLOP/s", "prefill TFLOP/s", "mfma"
         desc = f"{name}: B {p.B}, H {p.H}, H_kv {p.H_kv}, N {p.N}, d_qk {p.d_qk}, d_v {p.d_v}, {p.dtype}"
+        if win:
+            desc += f", causal window {win}"
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -217,7 +223,11 @@ def main():
                              "decode_v1", "copy"],
                     help="step: the whole path (default); otherwise time one workload alone "
                          "(copy: a plain device copy of 4 GiB, for calibrating HBM byte counters)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="causal sliding window for a single prefill workload (0 = none)")
     args = ap.parse_args()
+    if args.window and args.workload in ("step", "copy", "decode_v2", "decode_v1"):
+        ap.error("--window applies to a single prefill workload")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
               "(sharding is by (batch, KV head) with no communication; see the design notes)",

@@ -75,6 +75,7 @@ class DecodeArgs(ctypes.Structure):
         ("so", _c_int64_2),
         ("split_pages", ctypes.c_int),
         ("dev_err", ctypes.c_void_p),
+        ("window", ctypes.c_int),
     ]
 
 
@@ -207,7 +208,7 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool = True, norm: bo
 
 
 def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
-                 scale, out, split_pages, dev_err, k2_cache=None) -> DecodeArgs:
+                 scale, out, split_pages, dev_err, k2_cache=None, window=0) -> DecodeArgs:
     B, H, dqk = q1.shape
     P, Hkv, page, _ = k_cache.shape
     dv = v_cache.shape[3]
@@ -240,34 +241,35 @@ def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm
     a.so = _c_int64_2(out.stride(0), out.stride(1)) if out is not None else _c_int64_2(H * dv, dv)
     a.split_pages = int(split_pages)
     a.dev_err = _ptr(dev_err)
+    a.window = int(window)
     return a
 
 
 def decode_workspace_bytes(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int,
                            norm: bool = False, gamma=None, eps: float = 1e-5, scale: float = 0.0,
-                           split_pages: int = 0, k2_cache=None) -> int:
+                           split_pages: int = 0, k2_cache=None, window: int = 0) -> int:
     a = _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
-                     scale, None, split_pages, None, k2_cache)
+                     scale, None, split_pages, None, k2_cache, window)
     return int(load_library().diffattn_decode_workspace_bytes(ctypes.byref(a)))
 
 
 def decode(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int, norm: bool = False,
            gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, workspace=None,
-           split_pages: int = 0, dev_err=None, stream=None, k2_cache=None):
+           split_pages: int = 0, dev_err=None, stream=None, k2_cache=None, window: int = 0):
     """Paged decode (one query token per sequence).
 
     q1, q2 [B, H, d_qk]; k_cache [num_pages, H_kv, page, d_qk] and v_cache
     [num_pages, H_kv, page, d_v] contiguous; k_cache serves both branches
     unless k2_cache (the branch-2 keys, V1 form with d_qk 64) is given;
-    page_table [B, max_pages] int32; ctx_len [B] int32; lam [H] fp32.
-    Returns out [B, H, d_v]."""
+    page_table [B, max_pages] int32; ctx_len [B] int32; lam [H] fp32;
+    window > 0: the query sees its last window tokens. Returns out [B, H, d_v]."""
     import torch
     B, H, _ = q1.shape
     dv = v_cache.shape[3]
     if out is None:
         out = torch.empty((B, H, dv), dtype=q1.dtype, device=q1.device)
     a = _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
-                     scale, out, split_pages, dev_err, k2_cache)
+                     scale, out, split_pages, dev_err, k2_cache, window)
     lib = load_library()
     need = int(lib.diffattn_decode_workspace_bytes(ctypes.byref(a)))
     if workspace is None:

@@ -45,7 +45,9 @@
 // outside [0, num_pages) is never dereferenced: page 0 is read in its place,
 // all its tokens are masked and bit 0 of *dev_err is set. A sequence whose
 // length is out of range has no pages; its outputs are zeros and bit 1 of
-// *dev_err is set.
+// *dev_err is set. With a causal window W the query sees tokens L-W .. L-1
+// (lesson "Attention Variants", sliding window, for the last row): only the
+// pages holding them enter the page list and earlier tokens are masked.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -82,17 +84,24 @@ struct DecodeParams {
     int32_t *pref;  // workspace header: pages of the valid sequences before b, [B + 1]
     float *rec;     // workspace records, qrows * (kDV + 2) floats each
     int *dev_err;
-    int B, H, H_kv, group, qrows, max_pages, num_pages, target, num_wgs, norm;
+    int B, H, H_kv, group, qrows, max_pages, num_pages, target, num_wgs, norm, window;
     float sc_log2, eps, one_minus_init;
 };
 
 __device__ __forceinline__ uint4 ldg16(const __bf16 *p) { return *(const uint4 *)p; }
 
-// pages of sequence b; 0 for b >= B or a length out of range
+// first token the query sees: L - W with a window W < L, else 0
+__device__ __forceinline__ int first_token(const DecodeParams &p, int L) {
+    return (p.window > 0 && L > p.window) ? L - p.window : 0;
+}
+
+// pages of sequence b holding visible tokens (those from the page of its
+// first visible token on); 0 for b >= B or a length out of range
 __device__ __forceinline__ int seq_pages(const DecodeParams &p, int b) {
     if (b >= p.B) return 0;
     const int L = p.ctx_len[b];
-    return (L >= 1 && L <= p.max_pages * kPage) ? (L + kPage - 1) / kPage : 0;
+    if (L < 1 || L > p.max_pages * kPage) return 0;
+    return (L + kPage - 1) / kPage - first_token(p, L) / kPage;
 }
 
 // work-groups that share the T pages (each gets at least one)
@@ -188,10 +197,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int vswz = (vrow & 7) << 1;
 
     for (int64_t pos = start;;) {
-        // pages [p0, p1) of unit (b, g)
+        // pages [p0, p1) of unit (b, g), counted from the page of its first
+        // visible token (page index fp in the sequence)
         const int p0 = (int)(pos - ubase);
         const int p1 = (int)(min(end, ubase + c) - ubase);
         const int L = p.ctx_len[b];
+        const int t0 = first_token(p, L);
+        const int fp = t0 / kPage;
 
         // Q^T fragments: lane supplies query row n (pair n / 2, branch n % 2).
         // d_qk 128: k step kc covers features 32 kc + 8 grp .. +7 of the shared
@@ -221,7 +233,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         // pages in chunks of at most 64: a chunk's page ids are read once, one
         // per lane, and each page's id is then taken with v_readlane (a scalar),
         // so no vector load of the table sits between the K/V loads of pages
-        const int32_t *table = p.page_table + (int64_t)b * p.max_pages;
+        const int32_t *table = p.page_table + (int64_t)b * p.max_pages + fp;
         for (int c0 = p0; c0 < p1; c0 += 64) {
             const int np = min(64, p1 - c0);
             const int ids = lane < np ? table[c0 + lane] : 0;
@@ -249,13 +261,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
             };
 
             auto process = [&](const Slice &S, int k) {
-                const int pg = c0 + k;
-                const int vis = L - pg * kPage - 16 * wave;  // visible rows of this slice
+                const int pg = fp + c0 + k;                   // page index in the sequence
+                const int vis = L - pg * kPage - 16 * wave;   // rows >= vis are past the end
+                const int vlo = t0 - pg * kPage - 16 * wave;  // rows < vlo are before the window
                 // V rows into the wave buffer (rows past the end as zeros)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 4 * i + grp;
-                    const uint32_t keep = row < vis ? 0xffffffffu : 0u;  // select by value, not by address
+                    const uint32_t keep = (row < vis && row >= vlo) ? 0xffffffffu : 0u;  // select by value
                     uint4 v = S.v[i];
                     v.x &= keep;
                     v.y &= keep;
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 for (int kc = 0; kc < 4; ++kc) sc = mfma16(as_bf16x8(S.k[kc]), qf[kc], sc);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (!S.ok || 4 * grp + r >= vis) sc[r] = -INFINITY;
+                    if (!S.ok || 4 * grp + r >= vis || 4 * grp + r < vlo) sc[r] = -INFINITY;
                 float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
                 mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
                 mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -481,6 +494,7 @@ hipError_t launch_decode_bf16(const diffattn_decode_args &a, const DecodePlan &p
                     ? plan.max_wgs
                     : std::min(plan.max_wgs, kRounds * (d64 ? resident_split_wgs<64>() : resident_split_wgs<128>()));
     p.norm = a.norm == DIFFATTN_NORM_RMS;
+    p.window = a.window;
     p.sc_log2 = scale * kLog2e;
     p.eps = a.eps;
     p.one_minus_init = 1.0f - lambda_init;

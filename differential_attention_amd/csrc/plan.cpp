@@ -187,6 +187,7 @@ int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::str
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: scale must be finite and >= 0");
     if (a->norm == DIFFATTN_NORM_RMS && !(a->eps > 0.0f && !isinf(a->eps)))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: eps must be finite and > 0");
+    if (a->window < 0) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: window must be >= 0");
     if (a->split_pages < 0 || a->split_pages > kDecodeMaxTarget)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: split_pages must be in [0, 2^24]");
     if ((int64_t)a->B * a->max_pages > INT32_MAX)

@@ -108,6 +108,8 @@ typedef struct {
  * of all (sequence, KV head) pairs are cut into equal contiguous ranges, one
  * per work-group (at most 2048); 0 lets the library use one round of the
  * work-groups the device holds at once (at least 4 pages each).
+ * window: causal sliding window (0 = none); pages wholly before the window
+ * are neither counted nor read.
  * dev_err: optional device int; bit 0 is OR-ed in when a page id outside
  * [0, num_pages) is met, bit 1 when a ctx_len is out of range. Such pages or
  * sequences are skipped (never read). NULL disables the report (the checks
@@ -131,6 +133,7 @@ typedef struct {
     int64_t so[2];
     int split_pages;
     int *dev_err;
+    int window;          /* 0: none; W > 0: the query sees tokens ctx_len-W .. ctx_len-1 */
 } diffattn_decode_args;
 
 /*

@@ -57,7 +57,7 @@ def _load():
     lib.oracle_lambda.restype = None
     lib.oracle_prefill.argtypes = [P, P, P, P, P, i, i, i, i, i, i, P, i, i, i, d, i, P, d, P, i64, P]
     lib.oracle_prefill.restype = i
-    lib.oracle_decode.argtypes = [P, P, P, P, P, i, i, i, i, i, i, i, i, P, P, P, i, d, i, P, d, P]
+    lib.oracle_decode.argtypes = [P, P, P, P, P, i, i, i, i, i, i, i, i, P, P, P, i, i, d, i, P, d, P]
     lib.oracle_decode.restype = i
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
@@ -129,9 +129,11 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool, norm: bool,
 
 
 def decode(q1, q2, k1_cache, k2_cache, v_cache, page_table, ctx_len, lam, *, depth: int,
-           norm: bool, gamma=None, eps: float = 1e-5, scale: Optional[float] = None) -> np.ndarray:
+           norm: bool, gamma=None, eps: float = 1e-5, scale: Optional[float] = None,
+           window: int = 0) -> np.ndarray:
     """Paged decode: q1, q2 [B, H, d_qk]; caches [P, H_kv, page, d]; page_table
-    [B, max_pages] int32; ctx_len [B] int32; lam [H]. Returns [B, H, d_v] fp64."""
+    [B, max_pages] int32; ctx_len [B] int32; lam [H]; window 0 or W (the
+    query sees its last W tokens). Returns [B, H, d_v] fp64."""
     q1, q2, kc1, kc2, vc = (_f32(x) for x in (q1, q2, k1_cache, k2_cache, v_cache))
     B, H, dqk = q1.shape
     P, Hkv, page, _ = kc1.shape
@@ -146,7 +148,7 @@ def decode(q1, q2, k1_cache, k2_cache, v_cache, page_table, ctx_len, lam, *, dep
     out = np.empty((B, H, dv), np.float64)
     rc = _load().oracle_decode(_ptr(q1), _ptr(q2), _ptr(kc1), _ptr(kc2), _ptr(vc), B, H, Hkv, dqk, dv,
                                page, max_pages, P, _ptr(table), _ptr(ctx), _ptr(lam), int(depth),
-                               float(scale), int(bool(norm)), _ptr(g), float(eps), _ptr(out))
+                               int(window), float(scale), int(bool(norm)), _ptr(g), float(eps), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_decode: invalid argument or page id")
     return out

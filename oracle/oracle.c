@@ -199,16 +199,19 @@ int oracle_prefill(const float *q1, const float *q2, const float *k1,
  * Paged decode: one query token per sequence.
  *   q1, q2 [B, H, d_qk]; k1c, k2c [P, H_kv, page, d_qk]; vc [P, H_kv, page, d_v];
  *   page_table [B, max_pages]; ctx_len [B]; lambda [H]; gamma [H, d_v].
+ * window: 0 for none, else the query (token L-1) sees tokens L-W .. L-1
+ *   ([AV] causal window, read for the last row of a sequence).
  * out [B, H, d_v] fp64. Returns 0, or -1 on an invalid argument or page id.
  */
 int oracle_decode(const float *q1, const float *q2, const float *k1c,
                   const float *k2c, const float *vc, int B, int H, int H_kv,
                   int d_qk, int d_v, int page, int max_pages, int num_pages,
                   const int32_t *page_table, const int32_t *ctx_len,
-                  const double *lambda, int depth, double scale, int norm,
+                  const double *lambda, int depth, int window, double scale, int norm,
                   const float *gamma, double eps, double *out)
 {
     if (B < 0 || H <= 0 || H_kv <= 0 || d_qk <= 0 || d_v <= 0 || page <= 0) return -1;
+    if (window < 0) return -1;
     if (H % H_kv != 0) return -1;
     if (norm && !gamma) return -1;
     const int group = H / H_kv;
@@ -228,17 +231,18 @@ int oracle_decode(const float *q1, const float *q2, const float *k1c,
             int b = (int)(t / H), h = (int)(t % H), g = h / group;
             int64_t L = ctx_len[b];
             if (L < 0 || L > maxlen) { bad = 1; continue; }
+            int64_t lo = (window > 0 && L > window) ? L - window : 0; /* visible tokens [lo, L) */
             int ok = 1;
-            for (int64_t j = 0; j < L; ++j) {
+            for (int64_t j = lo; j < L; ++j) {
                 int32_t phys = page_table[(int64_t)b * max_pages + j / page];
                 if (phys < 0 || phys >= num_pages) { ok = 0; break; }
                 int64_t base = (((int64_t)phys * H_kv + g) * page + j % page);
-                kp1[j] = k1c + base * d_qk;
-                kp2[j] = k2c + base * d_qk;
-                vp[j] = vc + base * d_v;
+                kp1[j - lo] = k1c + base * d_qk;
+                kp2[j - lo] = k2c + base * d_qk;
+                vp[j - lo] = vc + base * d_v;
             }
             if (!ok) { bad = 1; continue; }
-            diff_row(q1 + t * d_qk, q2 + t * d_qk, kp1, kp2, vp, L, d_qk, d_v,
+            diff_row(q1 + t * d_qk, q2 + t * d_qk, kp1, kp2, vp, L - lo, d_qk, d_v,
                      lambda[h], scale, norm, norm ? gamma + (int64_t)h * d_v : NULL,
                      eps, init, s1, s2, out + t * d_v);
         }

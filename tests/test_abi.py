@@ -194,6 +194,7 @@ def test_decode_workspace_and_plan(lib):
     ("page_table", None, da.EINVAL),
     ("split_pages", -1, da.EINVAL),
     ("split_pages", (1 << 24) + 1, da.EINVAL),
+    ("window", -3, da.EINVAL),
     ("out", FAKE, da.EINVAL),           # overlaps q1
 ])
 def test_decode_rejects(lib, field, value, code):

@@ -47,7 +47,7 @@ class DecodeCase:
         args.update(kw)
         return self.da.decode(self.q1, self.q2, self.kc, self.vc, self.table, self.ctx, self.lam, **args)
 
-    def oracle(self, seqs=None, norm=None, gamma=None):
+    def oracle(self, seqs=None, norm=None, gamma=None, window=0):
         """Oracle on all sequences, or on a subset with their pages compacted."""
         d = self.d
         norm = d.norm if norm is None else norm
@@ -56,7 +56,8 @@ class DecodeCase:
         if seqs is None:
             kc, kc2 = d.f32("k1_cache"), d.f32("k2_cache")
             return oracle.decode(d.f32("q1"), d.f32("q2"), kc, kc2, d.f32("v_cache"), d.page_table,
-                                 d.ctx_len, self.lam64, depth=d.depth, norm=norm, gamma=gamma)
+                                 d.ctx_len, self.lam64, depth=d.depth, norm=norm, gamma=gamma,
+                                 window=window)
         seqs = np.asarray(seqs)
         npg = (d.ctx_len[seqs] + d.page - 1) // d.page
         used = np.concatenate([d.page_table[b, :n] for b, n in zip(seqs, npg)])
@@ -68,7 +69,7 @@ class DecodeCase:
         kc2 = W.bf16_to_f32(d.k2_cache[used])
         vc = W.bf16_to_f32(d.v_cache[used])
         return oracle.decode(d.f32("q1")[seqs], d.f32("q2")[seqs], kc, kc2, vc, table, d.ctx_len[seqs],
-                             self.lam64, depth=d.depth, norm=norm, gamma=gamma)
+                             self.lam64, depth=d.depth, norm=norm, gamma=gamma, window=window)
 
 
 def small(B=6, lens=None, H=8, H_kv=2, seed=0, max_pages=16):
@@ -253,3 +254,26 @@ def test_decode_v1_full(torch, da):
     out = c.run().float().cpu().numpy()
     seqs = np.array([0, 5, int(np.argmax(d.ctx_len)), int(np.argmin(d.ctx_len)), 40, 63])
     check(out[seqs], c.oracle(seqs=seqs), "bf16", "decode_v1 sampled sequences")
+
+
+# ---- causal sliding window: the query sees its last W tokens
+
+
+@pytest.mark.parametrize("form", ["v2", "v1"])
+@pytest.mark.parametrize("window", [1, 15, 64, 65, 200, 1000])
+@pytest.mark.parametrize("split_pages", [0, 2])
+def test_decode_sliding_window(torch, da, form, window, split_pages):
+    lens = [1, 63, 64, 65, 128, 1000, 333]
+    d = small_v1(lens, seed=50 + window) if form == "v1" else small(lens=lens, seed=50 + window)
+    c = DecodeCase(d, torch, da)
+    say(f"decode {form} window {window} split_pages {split_pages}")
+    check(c.run(window=window, split_pages=split_pages).float().cpu().numpy(), c.oracle(window=window),
+          "bf16", f"decode {form} W={window}")
+
+
+def test_decode_window_at_least_len_is_plain_bitwise(torch, da):
+    d = small(lens=[300, 64, 1000, 5], seed=60)
+    c = DecodeCase(d, torch, da)
+    plain = c.run().clone()
+    for w in (1000, 1024, 1 << 20):
+        assert torch.equal(c.run(window=w), plain), w

@@ -322,6 +322,30 @@ def test_decode_equals_last_prefill_row(L, page):
         np.testing.assert_allclose(dec, pre[:, :, -1], rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("L,page,window", [(13, 4, 1), (13, 4, 5), (16, 4, 8), (37, 8, 9), (37, 8, 37),
+                                           (37, 8, 100)])
+def test_decode_window_equals_last_windowed_prefill_row(L, page, window):
+    # the decode query is the last row of its sequence: with a window it sees
+    # tokens L-W..L-1, the last row of the windowed prefill
+    rng = np.random.default_rng(40 + L + window)
+    B, H, Hkv, d, dv = 2, 2, 1, 8, 6
+    q1, q2 = rnd(rng, B, H, L, d), rnd(rng, B, H, L, d)
+    k1, k2 = rnd(rng, B, Hkv, L, d), rnd(rng, B, Hkv, L, d)
+    v = rnd(rng, B, Hkv, L, dv)
+    lam = rng.uniform(-0.5, 1.2, H)
+    gamma = rng.uniform(0.9, 1.1, (H, dv)).astype(np.float32)
+    pre = _prefill(q1, q2, k1, k2, v, lam, depth=9, causal=True, norm=True, gamma=gamma, window=window)
+    kc1, vc, table = _paged(k1, v, page, np.random.default_rng(2))
+    kc2, _, _ = _paged(k2, v, page, np.random.default_rng(2))
+    dec = oracle.decode(q1[:, :, -1], q2[:, :, -1], kc1, kc2, vc, table, np.full(B, L, np.int32), lam,
+                        depth=9, norm=True, gamma=gamma, window=window)
+    np.testing.assert_allclose(dec, pre[:, :, -1], rtol=0, atol=1e-14)
+    if window >= L:  # no token outside the window: the plain decode, bit for bit
+        full = oracle.decode(q1[:, :, -1], q2[:, :, -1], kc1, kc2, vc, table, np.full(B, L, np.int32),
+                             lam, depth=9, norm=True, gamma=gamma)
+        assert np.array_equal(dec, full)
+
+
 def test_decode_page_permutation_invariance_and_brute():
     rng = np.random.default_rng(30)
     B, H, Hkv, d, dv, page = 3, 2, 1, 4, 3, 4
