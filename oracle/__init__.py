@@ -16,6 +16,9 @@ Parity status of each function (pins live in ``tests/test_oracle.py``):
                printed causal-mask figure, the signal-plus-noise toy)
   decode       pinned (equals the last row of causal prefill; page-table
                permutation invariance; brute force)
+  backward.prefill_backward, backward.lambda_backward (the gradients, fp64
+               numpy): pinned by central finite differences of the brute-force
+               forward and by invariants (tests/test_oracle_backward.py)
 """
 from __future__ import annotations
 
