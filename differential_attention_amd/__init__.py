@@ -51,6 +51,38 @@ class PrefillArgs(ctypes.Structure):
         ("out", ctypes.c_void_p),
         ("so", _c_int64_3),
         ("window", ctypes.c_int),
+        ("o1", ctypes.c_void_p), ("o2", ctypes.c_void_p),
+        ("lse1", ctypes.c_void_p), ("lse2", ctypes.c_void_p),
+    ]
+
+
+class BackwardArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("H_kv", ctypes.c_int), ("N", ctypes.c_int),
+        ("d_qk", ctypes.c_int), ("d_v", ctypes.c_int),
+        ("q1", ctypes.c_void_p), ("q2", ctypes.c_void_p),
+        ("k1", ctypes.c_void_p), ("k2", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("sq1", _c_int64_3), ("sq2", _c_int64_3), ("sk1", _c_int64_3), ("sk2", _c_int64_3),
+        ("sv", _c_int64_3),
+        ("lambda_", ctypes.c_void_p),
+        ("depth", ctypes.c_int),
+        ("causal", ctypes.c_int),
+        ("window", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("norm", ctypes.c_int),
+        ("gamma", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("o1", ctypes.c_void_p), ("o2", ctypes.c_void_p),
+        ("lse1", ctypes.c_void_p), ("lse2", ctypes.c_void_p),
+        ("dout", ctypes.c_void_p),
+        ("sdo", _c_int64_3),
+        ("dq1", ctypes.c_void_p), ("dq2", ctypes.c_void_p),
+        ("dk1", ctypes.c_void_p), ("dk2", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p),
+        ("dlambda", ctypes.c_void_p),
+        ("dgamma", ctypes.c_void_p),
     ]
 
 
@@ -108,6 +140,12 @@ def load_library(path: Optional[str] = None):
     lib.diffattn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.diffattn_decode.argtypes = [ctypes.POINTER(DecodeArgs), V, ctypes.c_size_t, V]
     lib.diffattn_decode.restype = I
+    lib.diffattn_backward_workspace_bytes.argtypes = [ctypes.POINTER(BackwardArgs)]
+    lib.diffattn_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.diffattn_backward.argtypes = [ctypes.POINTER(BackwardArgs), V, ctypes.c_size_t, V]
+    lib.diffattn_backward.restype = I
+    lib.diffattn_lambda_backward.argtypes = [V, V, V, V, I, I, V, V, V, V, V, V]
+    lib.diffattn_lambda_backward.restype = I
     lib.diffattn_last_error.argtypes = []
     lib.diffattn_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -169,14 +207,17 @@ def _strides3(t):
 
 
 def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool = True, norm: bool = False,
-            gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, stream=None, window: int = 0):
+            gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, stream=None, window: int = 0,
+            stats=None):
     """Differential-attention prefill.
 
     q1, q2 [B, H, N, d_qk]; k1, k2 [B, H_kv, N, d_qk] (pass the same tensor
     for both in the V2 form); v [B, H_kv, N, d_v]; lam [H] fp32 device;
     gamma [H, d_v] fp32 device when norm (V1). Views with unit innermost
     stride are accepted as they are. window > 0 (causal only) limits row i to
-    keys i-window+1 .. i. Returns out [B, H, N, d_v]."""
+    keys i-window+1 .. i. stats: None, or a tuple (o1, o2, lse1, lse2) of fp32
+    tensors [B, H, N, d_v] x 2 and [B, H, N] x 2 that receive the statistics
+    the backward pass needs (see prefill_stats). Returns out [B, H, N, d_v]."""
     import torch
     B, H, N, dqk = q1.shape
     Hkv, dv = k1.shape[1], v.shape[3]
@@ -198,6 +239,11 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool = True, norm: bo
     a.depth = int(depth)
     a.causal = int(bool(causal))
     a.window = int(window)
+    if stats is not None:
+        for t, shape in zip(stats, ((B, H, N, dv), (B, H, N, dv), (B, H, N), (B, H, N))):
+            if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError(f"stats tensors must be contiguous fp32 of shapes {shape}")
+        a.o1, a.o2, a.lse1, a.lse2 = (_ptr(t) for t in stats)
     a.scale = float(scale)
     a.norm = NORM_RMS if norm else NORM_NONE
     a.gamma = _ptr(gamma) if norm else None
@@ -205,6 +251,73 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool = True, norm: bo
     a.out = _ptr(out)
     _check(load_library().diffattn_prefill(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def prefill_stats(q1, v):
+    """Fresh (o1, o2, lse1, lse2) tensors for prefill(..., stats=...)."""
+    import torch
+    B, H, N, _ = q1.shape
+    dv = v.shape[3]
+    f = lambda *s: torch.empty(s, dtype=torch.float32, device=q1.device)
+    return f(B, H, N, dv), f(B, H, N, dv), f(B, H, N), f(B, H, N)
+
+
+def backward(q1, q2, k1, k2, v, lam, stats, dout, *, depth: int, causal: bool = True, norm: bool = False,
+             gamma=None, eps: float = 1e-5, scale: float = 0.0, window: int = 0, workspace=None, stream=None):
+    """Gradients of prefill(q1, q2, k1, k2, v, lam, ...) given dout (bf16
+    [B, H, N, d_v]) and the statistics (o1, o2, lse1, lse2) a prefill call with
+    stats=... stored. Returns a dict of fp32 tensors dq1, dq2, dk1, dk2, dv,
+    dlambda and (norm) dgamma; with k1 is k2 (one key tensor) dk1 is the whole
+    key gradient and dk2 is the same tensor."""
+    import torch
+    B, H, N, dqk = q1.shape
+    Hkv, dv_ = k1.shape[1], v.shape[3]
+    shared = k1.data_ptr() == k2.data_ptr() and k1.stride() == k2.stride()
+    f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=q1.device)
+    g = {"dq1": f(B, H, N, dqk), "dq2": f(B, H, N, dqk), "dk1": f(B, Hkv, N, dqk), "dv": f(B, Hkv, N, dv_),
+         "dlambda": f(H)}
+    g["dk2"] = g["dk1"] if shared else f(B, Hkv, N, dqk)
+    g["dgamma"] = f(H, dv_) if norm else None
+    a = BackwardArgs()
+    a.dtype = _dtype_code(q1)
+    a.B, a.H, a.H_kv, a.N, a.d_qk, a.d_v = B, H, Hkv, N, dqk, dv_
+    for t in (q2, k1, k2, v, dout):
+        if t.dtype != q1.dtype:
+            raise ValueError("all inputs must share one dtype")
+    a.q1, a.q2, a.k1, a.k2, a.v = (_ptr(t) for t in (q1, q2, k1, k2, v))
+    a.sq1, a.sq2 = _c_int64_3(*_strides3(q1)), _c_int64_3(*_strides3(q2))
+    a.sk1, a.sk2 = _c_int64_3(*_strides3(k1)), _c_int64_3(*_strides3(k2))
+    a.sv = _c_int64_3(*_strides3(v))
+    a.lambda_ = _ptr(lam)
+    a.depth, a.causal, a.window, a.scale = int(depth), int(bool(causal)), int(window), float(scale)
+    a.norm = NORM_RMS if norm else NORM_NONE
+    a.gamma = _ptr(gamma) if norm else None
+    a.eps = float(eps)
+    for t in stats:
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("stats must be contiguous fp32 tensors")
+    a.o1, a.o2, a.lse1, a.lse2 = (_ptr(t) for t in stats)
+    a.dout = _ptr(dout)
+    a.sdo = _c_int64_3(*_strides3(dout))
+    a.dq1, a.dq2, a.dk1, a.dv, a.dlambda = (_ptr(g[k]) for k in ("dq1", "dq2", "dk1", "dv", "dlambda"))
+    a.dk2 = None if shared else _ptr(g["dk2"])
+    a.dgamma = _ptr(g["dgamma"]) if norm else None
+    lib = load_library()
+    need = int(lib.diffattn_backward_workspace_bytes(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q1.device)
+    _check(lib.diffattn_backward(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return g
+
+
+def lambda_backward(lq1, lk1, lq2, lk2, dlambda, stream=None):
+    """Gradients of the four [H, d_lambda] lambda vectors given dlambda [H]."""
+    import torch
+    H, dl = lq1.shape
+    outs = [torch.empty_like(lq1) for _ in range(4)]
+    _check(load_library().diffattn_lambda_backward(_ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), H, dl,
+                                                   _ptr(dlambda), *(_ptr(t) for t in outs), _stream(stream)))
+    return dict(zip(("dlq1", "dlk1", "dlq2", "dlk2"), outs))
 
 
 def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,

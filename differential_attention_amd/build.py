@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 
-HIP_SOURCES = ["lambda.hip", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip"]
+HIP_SOURCES = ["lambda.hip", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip", "backward.hip"]
 HOST_SOURCES = ["api.cpp"]      # host code that calls the HIP runtime
 PLAIN_SOURCES = ["plan.cpp"]    # host code with no HIP dependency
 

@@ -86,4 +86,43 @@ int diffattn_decode(const diffattn_decode_args *a, void *workspace, size_t ws_by
     return hip_status(e, "diffattn_decode");
 }
 
+size_t diffattn_backward_workspace_bytes(const diffattn_backward_args *a) {
+    da::BackwardPlan plan;
+    std::string msg;
+    if (da::check_backward_sizes(a, &plan, &msg) != DIFFATTN_OK) return 0;
+    return plan.ws_bytes;
+}
+
+int diffattn_backward(const diffattn_backward_args *a, void *workspace, size_t ws_bytes, void *stream) {
+    std::string msg;
+    da::BackwardPlan plan;
+    int rc = da::check_backward(a, &plan, &msg);
+    if (rc != DIFFATTN_OK) return set_error(rc, msg);
+    if (plan.empty) {
+        g_last_error.clear();
+        return DIFFATTN_OK;
+    }
+    if (!workspace || ws_bytes < plan.ws_bytes)
+        return set_error(DIFFATTN_EWORKSPACE, "diffattn_backward: workspace missing or smaller than "
+                                              "diffattn_backward_workspace_bytes()");
+    if (((uintptr_t)workspace % 256) != 0)
+        return set_error(DIFFATTN_EWORKSPACE, "diffattn_backward: workspace must be 256-byte aligned");
+    const float scale = a->scale > 0.0f ? a->scale : (float)(1.0 / sqrt((double)a->d_qk));
+    hipError_t e = da::launch_backward_bf16(*a, plan, workspace, scale, (float)da::lambda_init(a->depth),
+                                            (hipStream_t)stream);
+    return hip_status(e, "diffattn_backward");
+}
+
+int diffattn_lambda_backward(const float *lq1, const float *lk1, const float *lq2, const float *lk2, int H,
+                             int d_lambda, const float *dlambda, float *dlq1, float *dlk1, float *dlq2,
+                             float *dlk2, void *stream) {
+    if (!lq1 || !lk1 || !lq2 || !lk2 || !dlambda || !dlq1 || !dlk1 || !dlq2 || !dlk2)
+        return set_error(DIFFATTN_EINVAL, "diffattn_lambda_backward: null pointer");
+    if (H < 1 || d_lambda < 1 || d_lambda > 4096)
+        return set_error(DIFFATTN_EINVAL, "diffattn_lambda_backward: need H >= 1 and 1 <= d_lambda <= 4096");
+    hipError_t e = da::launch_lambda_backward(lq1, lk1, lq2, lk2, H, d_lambda, dlambda, dlq1, dlk1, dlq2, dlk2,
+                                              (hipStream_t)stream);
+    return hip_status(e, "diffattn_lambda_backward");
+}
+
 }  // extern "C"

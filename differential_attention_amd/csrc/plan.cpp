@@ -2,6 +2,7 @@
 #include "plan.hpp"
 
 #include <math.h>
+#include <string.h>
 
 #include <algorithm>
 #include <vector>
@@ -99,6 +100,9 @@ int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string
     if (a->causal != 0 && a->causal != 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: causal must be 0 or 1");
     if (a->window < 0 || (a->window > 0 && !a->causal))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: window must be 0, or > 0 with causal");
+    const int nstats = (a->o1 != nullptr) + (a->o2 != nullptr) + (a->lse1 != nullptr) + (a->lse2 != nullptr);
+    if (nstats != 0 && nstats != 4)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: set all of o1, o2, lse1, lse2 or none");
     if (a->norm != DIFFATTN_NORM_NONE && a->norm != DIFFATTN_NORM_RMS)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: unknown norm");
     if (!(a->scale >= 0.0f) || isinf(a->scale))
@@ -164,6 +168,22 @@ int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string
     if (a->norm == DIFFATTN_NORM_RMS) {
         Extent g{(uintptr_t)a->gamma, (uintptr_t)a->gamma + (uintptr_t)a->H * a->d_v * 4};
         if (overlaps(ext[5], g)) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: out overlaps gamma");
+    }
+    if (a->o1) {
+        const uintptr_t rows = (uintptr_t)a->B * a->H * a->N;
+        Extent st[4] = {{(uintptr_t)a->o1, (uintptr_t)a->o1 + rows * a->d_v * 4},
+                        {(uintptr_t)a->o2, (uintptr_t)a->o2 + rows * a->d_v * 4},
+                        {(uintptr_t)a->lse1, (uintptr_t)a->lse1 + rows * 4},
+                        {(uintptr_t)a->lse2, (uintptr_t)a->lse2 + rows * 4}};
+        if (!aligned(a->o1, 16) || !aligned(a->o2, 16) || !aligned(a->lse1, 4) || !aligned(a->lse2, 4))
+            return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: statistics misaligned");
+        for (int x = 0; x < 4; ++x) {
+            for (int y = x + 1; y < 4; ++y)
+                if (overlaps(st[x], st[y])) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: statistics overlap");
+            for (int t = 0; t < 6; ++t)
+                if (overlaps(st[x], ext[t]))
+                    return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: statistics overlap an input or out");
+        }
     }
     plan->shared_k = a->k1 == a->k2 && a->sk1[0] == a->sk2[0] && a->sk1[1] == a->sk2[1] &&
                      a->sk1[2] == a->sk2[2];
@@ -264,6 +284,142 @@ int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *m
         std::vector<Dim> qd = {{a->B, qstr[i][0]}, {a->H, qstr[i][1]}, {a->d_qk, 1}};
         if (!extent_of(qs[i], 2, qd, &e)) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: bad q strides");
         if (overlaps(eo, e)) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: out overlaps q");
+    }
+    return DIFFATTN_OK;
+}
+
+namespace {
+
+diffattn_prefill_args prefill_view(const diffattn_backward_args *a) {
+    diffattn_prefill_args p;
+    memset(&p, 0, sizeof(p));
+    p.dtype = a->dtype;
+    p.B = a->B;
+    p.H = a->H;
+    p.H_kv = a->H_kv;
+    p.N = a->N;
+    p.d_qk = a->d_qk;
+    p.d_v = a->d_v;
+    p.q1 = a->q1;
+    p.q2 = a->q2;
+    p.k1 = a->k1;
+    p.k2 = a->k2;
+    p.v = a->v;
+    for (int i = 0; i < 3; ++i) {
+        p.sq1[i] = a->sq1[i];
+        p.sq2[i] = a->sq2[i];
+        p.sk1[i] = a->sk1[i];
+        p.sk2[i] = a->sk2[i];
+        p.sv[i] = a->sv[i];
+        p.so[i] = a->sdo[i];
+    }
+    p.lambda = a->lambda;
+    p.depth = a->depth;
+    p.causal = a->causal;
+    p.window = a->window;
+    p.scale = a->scale;
+    p.norm = a->norm;
+    p.gamma = a->gamma;
+    p.eps = a->eps;
+    p.out = const_cast<void *>(a->dout);  // validated like an output: shape, strides, no overlap
+    return p;
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+int backward_common(const diffattn_backward_args *a, BackwardPlan *plan, std::string *msg, bool pointers) {
+    *plan = BackwardPlan();
+    if (!a) return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: null argument struct");
+    // the inputs are those of a prefill (dout standing in for its output);
+    // sizes only: the same checks on an empty batch, which stop before pointers
+    diffattn_prefill_args pa = prefill_view(a);
+    if (!pointers && pa.B > 0) pa.B = 0;
+    PrefillPlan pp;
+    std::string m;
+    const int rc = check_prefill(&pa, &pp, &m);
+    if (rc != DIFFATTN_OK) {
+        std::string t = m;
+        const std::string from = "diffattn_prefill";
+        if (t.compare(0, from.size(), from) == 0) t = "diffattn_backward" + t.substr(from.size());
+        return fail(msg, rc, t);
+    }
+    if (a->dtype != DIFFATTN_BF16)
+        return fail(msg, DIFFATTN_EUNSUPPORTED, "diffattn_backward: supports bf16 inputs");
+    plan->shared_k = a->k1 == a->k2 && a->sk1[0] == a->sk2[0] && a->sk1[1] == a->sk2[1] && a->sk1[2] == a->sk2[2];
+    plan->rows = (int64_t)a->B * a->H * a->N;
+    plan->prep_blocks = (int64_t)a->B * a->H * ((a->N + kBwdPrepRows - 1) / kBwdPrepRows);
+    plan->empty = a->B == 0 || a->N == 0;
+    size_t off = 0;
+    plan->off_dy = off;
+    off += round256((size_t)plan->rows * a->d_v * 2);
+    plan->off_dt1 = off;
+    off += round256((size_t)plan->rows * 4);
+    plan->off_dt2 = off;
+    off += round256((size_t)plan->rows * 4);
+    plan->off_part = off;
+    off += round256((size_t)plan->prep_blocks * (1 + a->d_v) * 4);
+    plan->ws_bytes = plan->empty ? 0 : off;
+    return DIFFATTN_OK;
+}
+
+}  // namespace
+
+int check_backward_sizes(const diffattn_backward_args *a, BackwardPlan *plan, std::string *msg) {
+    return backward_common(a, plan, msg, false);
+}
+
+int check_backward(const diffattn_backward_args *a, BackwardPlan *plan, std::string *msg) {
+    int rc = backward_common(a, plan, msg, true);
+    if (rc != DIFFATTN_OK || plan->empty) return rc;
+    if (!a->o1 || !a->o2 || !a->lse1 || !a->lse2 || !a->dout)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: null statistics or dout");
+    if (!a->dq1 || !a->dq2 || !a->dk1 || !a->dv || !a->dlambda)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: null gradient output");
+    if (plan->shared_k) {
+        if (a->dk2 && a->dk2 != a->dk1)
+            return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: with one key tensor dk2 must be NULL or dk1");
+    } else if (!a->dk2 || a->dk2 == a->dk1) {
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: two key tensors need two key gradients");
+    }
+    if (a->norm == DIFFATTN_NORM_RMS && !a->dgamma)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: RMS norm needs dgamma");
+    const void *al16[] = {a->o1, a->o2, a->dq1, a->dq2, a->dk1, a->dk2 ? a->dk2 : a->dk1, a->dv};
+    for (const void *p : al16)
+        if (!aligned(p, 16)) return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: fp32 tensor not 16-byte aligned");
+    if (!aligned(a->lse1, 4) || !aligned(a->lse2, 4) || !aligned(a->dlambda, 4) ||
+        (a->dgamma && !aligned(a->dgamma, 4)))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: fp32 array misaligned");
+
+    // outputs must not overlap each other or any input
+    const uintptr_t rows = (uintptr_t)plan->rows;
+    const uintptr_t kvrows = (uintptr_t)a->B * a->H_kv * a->N;
+    auto E = [](const void *p, uintptr_t bytes) { return Extent{(uintptr_t)p, (uintptr_t)p + bytes}; };
+    std::vector<Extent> outs = {E(a->dq1, rows * a->d_qk * 4), E(a->dq2, rows * a->d_qk * 4),
+                                E(a->dk1, kvrows * a->d_qk * 4), E(a->dv, kvrows * a->d_v * 4),
+                                E(a->dlambda, (uintptr_t)a->H * 4)};
+    if (!plan->shared_k) outs.push_back(E(a->dk2, kvrows * a->d_qk * 4));
+    if (a->norm == DIFFATTN_NORM_RMS) outs.push_back(E(a->dgamma, (uintptr_t)a->H * a->d_v * 4));
+    std::vector<Extent> ins = {E(a->o1, rows * a->d_v * 4), E(a->o2, rows * a->d_v * 4), E(a->lse1, rows * 4),
+                               E(a->lse2, rows * 4), E(a->lambda, (uintptr_t)a->H * 4)};
+    if (a->norm == DIFFATTN_NORM_RMS && a->gamma) ins.push_back(E(a->gamma, (uintptr_t)a->H * a->d_v * 4));
+    // the strided bf16 inputs, by their extents
+    struct T {
+        const void *p;
+        const int64_t *s;
+        int64_t h, d;
+    } ts[] = {{a->q1, a->sq1, a->H, a->d_qk}, {a->q2, a->sq2, a->H, a->d_qk}, {a->k1, a->sk1, a->H_kv, a->d_qk},
+              {a->k2, a->sk2, a->H_kv, a->d_qk}, {a->v, a->sv, a->H_kv, a->d_v}, {a->dout, a->sdo, a->H, a->d_v}};
+    for (const T &t : ts) {
+        Extent e;
+        std::vector<Dim> dims = {{a->B, t.s[0]}, {t.h, t.s[1]}, {a->N, t.s[2]}, {t.d, 1}};
+        if (!extent_of(t.p, 2, dims, &e)) return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: bad strides");
+        ins.push_back(e);
+    }
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(outs[i], outs[j])) return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: gradient outputs overlap");
+        for (const Extent &e : ins)
+            if (overlaps(outs[i], e)) return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: a gradient overlaps an input");
     }
     return DIFFATTN_OK;
 }

@@ -41,6 +41,27 @@ struct PrefillPlan {
     bool empty = false;     // nothing to compute (B == 0 or N == 0)
 };
 
+// Backward plan: the workspace holds the output gradient after the norm
+// (bf16, one d_v row per query row), two per-row reductions (rowsum of the
+// output gradient times each branch's normalised output) and, per block of
+// kBwdPrepRows rows, the partial sums of dlambda and dgamma.
+constexpr int kBwdPrepRows = 4;
+
+struct BackwardPlan {
+    bool shared_k = false;
+    bool empty = false;
+    int64_t rows = 0;        // B * H * N
+    int64_t prep_blocks = 0; // B * H * ceil(N / kBwdPrepRows)
+    size_t off_dy = 0, off_dt1 = 0, off_dt2 = 0, off_part = 0;
+    size_t ws_bytes = 0;
+};
+
+// Validate backward sizes and flags (no pointer examined) and build the plan.
+int check_backward_sizes(const diffattn_backward_args *a, BackwardPlan *plan, std::string *msg);
+
+// Validate backward arguments (workspace excluded) and build the plan.
+int check_backward(const diffattn_backward_args *a, BackwardPlan *plan, std::string *msg);
+
 // lambda_init(depth) = 0.8 - 0.6 exp(-0.3 (depth - 1)); NaN for depth < 1.
 double lambda_init(int depth);
 

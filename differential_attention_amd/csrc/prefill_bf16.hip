@@ -51,8 +51,8 @@
 // the number of (batch, KV head) units is a multiple of 8, all work-groups
 // reading one KV head are placed on the same XCD so its K/V stay in that
 // XCD's L2.
-#include "common.hpp"
 #include "launch.hpp"
+#include "tiles.hpp"
 
 #include <climits>
 
@@ -60,14 +60,8 @@ namespace da {
 
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int kDV = 128;              // value width (both forms)
 constexpr int kBM = 128;              // query rows per work-group
 constexpr int kWM = 32;               // query rows per wave
-constexpr int kBN = 64;               // keys per LDS tile
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
 // branch-split decomposition for a head dimension (see the header comment)
@@ -84,46 +78,10 @@ struct Bf16Params {
     int64_t sq1[3], sq2[3], sk1[3], sk2[3], sv[3], so[3];
     const float *lambda, *gamma;
     __bf16 *out;
+    float *o1, *o2, *lse1, *lse2;  // optional statistics for the backward pass (all or none)
     int B, H, H_kv, group, N, causal, window, row_blocks, xcd_units;
     float sc_log2;  // scale * log2(e)
     float eps, one_minus_init;
-};
-
-// Physical key (within a 32-key sub-block) read by the A-operand row m:
-// swap bits 2 and 3 of m.
-__device__ __forceinline__ int perm_key(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-// Key offset (within a sub-block, before adding 8 * lane-half) held by
-// register r of an S^T accumulator.
-__device__ __forceinline__ constexpr int key_of_reg(int r) { return 16 * ((r >> 3) & 1) + 4 * ((r >> 2) & 1) + (r & 3); }
-
-// XOR swizzle of the 16-byte chunk index inside a K-tile row (row bytes
-// 2 * DQK): keeps the 16 lanes of one ds_read_b128 pass on distinct banks.
-template <int DQK>
-__device__ __forceinline__ int k_swz(int row) {
-    return DQK == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-// XOR swizzle of the chunk index inside a V-tile row (256 bytes): the four
-// rows read by one ds_read_b64_tr_b16 pass land on distinct banks.
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
-
-__device__ __forceinline__ uint4 ldg16(const __bf16 *p) { return *(const uint4 *)p; }
-
-__device__ __forceinline__ void wait_vmem_all() {
-    // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-template <int DQK, bool SHARED_K>
-struct Tile {
-    static constexpr int kKBytes = kBN * DQK * 2;           // one K tile
-    static constexpr int kVBytes = kBN * kDV * 2;           // the V tile
-    static constexpr int kNK = SHARED_K ? 1 : 2;            // K tiles per stage
-    static constexpr int kStage = kNK * kKBytes + kVBytes;  // bytes per stage
-    static constexpr int kKCh = DQK / 8;                    // 16-byte chunks per K row
-    static constexpr int kKBlocks = kNK * kKBytes / 1024;   // 1 KB blocks of K per stage
-    static constexpr int kBlocks = kStage / 1024;           // 1 KB blocks per stage
-    static constexpr int kRowsPerKBlock = 1024 / (2 * DQK);
 };
 
 template <int DQK, bool SHARED_K, bool NORM, bool WIN>
@@ -382,6 +340,26 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     // ---- epilogue: y = O1 / l1 - lambda O2 / l2 (then the V1 norm), bf16 store
 #pragma unroll
     for (int j = 0; j < NBR; ++j) l[j] = halves_sum(l[j]);
+    // statistics for the backward pass: each branch's normalised output and
+    // natural-log log-sum-exp of its scaled scores (m is in log2 units)
+    if (p.o1 && myrow < p.N) {
+        const int64_t rowid = ((int64_t)b * p.H + h) * p.N + myrow;
+#pragma unroll
+        for (int j = 0; j < NBR; ++j) {
+            const int brj = br0 + j;
+            float *ob = (brj ? p.o2 : p.o1) + rowid * kDV + 4 * hh;
+            const float rl = 1.0f / l[j];
+#pragma unroll
+            for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const float4 v4 = {o[j][dc][4 * rq] * rl, o[j][dc][4 * rq + 1] * rl, o[j][dc][4 * rq + 2] * rl,
+                                       o[j][dc][4 * rq + 3] * rl};
+                    *(float4 *)(ob + 32 * dc + 8 * rq) = v4;
+                }
+            if (hh == 0) (brj ? p.lse2 : p.lse1)[rowid] = (m[j] + log2f(l[j])) * 0.69314718055994531f;
+        }
+    }
     f32x16 y[4];
     if constexpr (S::kOn) {
         // branch-2 waves hand lambda O2 / l2 to their branch-1 partner through LDS
@@ -487,6 +465,10 @@ hipError_t launch_prefill_bf16(const diffattn_prefill_args &a, float scale, floa
     p.lambda = a.lambda;
     p.gamma = a.gamma;
     p.out = (__bf16 *)a.out;
+    p.o1 = a.o1;
+    p.o2 = a.o2;
+    p.lse1 = a.lse1;
+    p.lse2 = a.lse2;
     p.B = a.B;
     p.H = a.H;
     p.H_kv = a.H_kv;

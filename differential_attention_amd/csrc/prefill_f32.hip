@@ -25,6 +25,7 @@ struct PrefillF32Params {
     int64_t sq1[3], sq2[3], sk1[3], sk2[3], sv[3], so[3];
     const float *lambda, *gamma;
     float *out;
+    float *o1, *o2, *lse1, *lse2;  // optional statistics for the backward pass (all or none)
     int H, group, N, d_qk, d_v, causal, window, norm;
     float scale, eps, one_minus_init;
 };
@@ -95,6 +96,23 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillF32Params p) {
     l1 = wave_sum(l1);
     l2 = wave_sum(l2);
 
+    if (p.o1) {
+        // each branch's normalised output and natural-log log-sum-exp
+        const int64_t rowid = ((int64_t)b * p.H + h) * p.N + i;
+        float *a1 = p.o1 + rowid * p.d_v, *a2 = p.o2 + rowid * p.d_v;
+        if (c0 < p.d_v) {
+            a1[c0] = o1a / l1;
+            a2[c0] = o2a / l2;
+        }
+        if (c1 < p.d_v) {
+            a1[c1] = o1b / l1;
+            a2[c1] = o2b / l2;
+        }
+        if (lane == 0) {
+            p.lse1[rowid] = m1 + logf(l1);
+            p.lse2[rowid] = m2 + logf(l2);
+        }
+    }
     const float lam = p.lambda[h];
     const float r1 = 1.0f / l1, r2 = lam / l2;
     float ya, yb;
@@ -133,6 +151,10 @@ hipError_t launch_prefill_f32(const diffattn_prefill_args &a, float scale, float
     p.lambda = a.lambda;
     p.gamma = a.gamma;
     p.out = (float *)a.out;
+    p.o1 = a.o1;
+    p.o2 = a.o2;
+    p.lse1 = a.lse1;
+    p.lse2 = a.lse2;
     p.H = a.H;
     p.group = a.H / a.H_kv;
     p.N = a.N;

@@ -85,6 +85,12 @@ typedef struct {
     void *out;
     int64_t so[3];
     int window;          /* 0: none; W > 0 (causal only): row i sees keys i-W+1 .. i */
+    /* Optional statistics for the backward pass (all four set, or all NULL):
+     * o1, o2 fp32 [B, H, N, d_v] contiguous: each branch's normalised output
+     * softmax(Q_k K_k^T scale) V; lse1, lse2 fp32 [B, H, N] contiguous: the
+     * natural-log log-sum-exp of each branch's scaled, masked scores per row. */
+    float *o1, *o2;
+    float *lse1, *lse2;
 } diffattn_prefill_args;
 
 /*
@@ -170,6 +176,66 @@ size_t diffattn_decode_workspace_bytes(const diffattn_decode_args *a);
  * workspace must be ordered on one stream.
  */
 int diffattn_decode(const diffattn_decode_args *a, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Backward pass of the prefill (the gradients of the function defined above;
+ * the pages give the forward only, the gradients follow from it by the chain
+ * rule). Inputs as in diffattn_prefill_args (bf16, d_v 128, d_qk 64 or 128),
+ * plus:
+ *   o1, o2, lse1, lse2  the statistics a diffattn_prefill call with the same
+ *                       inputs stored (fp32, contiguous)
+ *   dout, sdo[3]        gradient of the output [B, H, N, d_v], bf16, strides (b, h, n)
+ * Outputs (fp32, contiguous, overwritten):
+ *   dq1, dq2  [B, H, N, d_qk]
+ *   dk1, dk2  [B, H_kv, N, d_qk]; when k1 == k2 (one key tensor for both
+ *             branches) dk1 receives the whole key gradient and dk2 must be
+ *             NULL or equal to dk1
+ *   dv        [B, H_kv, N, d_v]
+ *   dlambda   [H]           (feed diffattn_lambda_backward for the four vectors)
+ *   dgamma    [H, d_v]      (RMS norm only; may be NULL otherwise)
+ * The workspace (diffattn_backward_workspace_bytes) holds the output gradient
+ * after the norm in bf16 and per-row reductions; 256-byte aligned.
+ */
+typedef struct {
+    int dtype;
+    int B, H, H_kv, N, d_qk, d_v;
+    const void *q1, *q2;
+    const void *k1, *k2;
+    const void *v;
+    int64_t sq1[3], sq2[3], sk1[3], sk2[3], sv[3];
+    const float *lambda;
+    int depth;
+    int causal;
+    int window;
+    float scale;
+    int norm;
+    const float *gamma;
+    float eps;
+    const float *o1, *o2;
+    const float *lse1, *lse2;
+    const void *dout;
+    int64_t sdo[3];
+    float *dq1, *dq2;
+    float *dk1, *dk2;
+    float *dv;
+    float *dlambda;
+    float *dgamma;
+} diffattn_backward_args;
+
+/* Workspace bytes for diffattn_backward (sizes only; 0 if invalid). */
+size_t diffattn_backward_workspace_bytes(const diffattn_backward_args *a);
+
+int diffattn_backward(const diffattn_backward_args *a, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Gradients of lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init with
+ * respect to the four [H, d_lambda] fp32 vectors, given dlambda [H]:
+ * dlq1 = dlambda e1 lk1, dlk1 = dlambda e1 lq1, dlq2 = -dlambda e2 lk2,
+ * dlk2 = -dlambda e2 lq2 with e_k = exp(lq_k . lk_k). Device pointers.
+ */
+int diffattn_lambda_backward(const float *lq1, const float *lk1, const float *lq2, const float *lk2, int H,
+                             int d_lambda, const float *dlambda, float *dlq1, float *dlk1, float *dlq2,
+                             float *dlk2, void *stream);
 
 /* Message for the last failure on this thread ("" if none). */
 const char *diffattn_last_error(void);

@@ -44,7 +44,9 @@ def test_exports_every_declared_symbol(lib):
 def test_struct_layout_matches_header(tmp_path):
     """ctypes mirrors of the argument structs have the C compiler's layout."""
     src = ["#include <stdio.h>", "#include <stddef.h>", '#include "diffattn.h"', "int main(void) {"]
-    for cname, py in (("diffattn_prefill_args", da.PrefillArgs), ("diffattn_decode_args", da.DecodeArgs)):
+    structs = (("diffattn_prefill_args", da.PrefillArgs), ("diffattn_decode_args", da.DecodeArgs),
+               ("diffattn_backward_args", da.BackwardArgs))
+    for cname, py in structs:
         src.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
         for fname, _ in py._fields_:
             cf = "lambda" if fname == "lambda_" else fname
@@ -55,7 +57,7 @@ def test_struct_layout_matches_header(tmp_path):
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)])
     out = subprocess.check_output([str(exe)], text=True).split("\n")
-    pys = {"diffattn_prefill_args": da.PrefillArgs, "diffattn_decode_args": da.DecodeArgs}
+    pys = dict(structs)
     for line in filter(None, out):
         cname, field, value = line.split()
         py = pys[cname]
@@ -222,3 +224,66 @@ def test_decode_workspace_needs_no_pointers(lib):
     assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) > 0
     a = _decode_args(H=36)   # invalid sizes still give 0
     assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def _backward_args(**kw):
+    a = da.BackwardArgs()
+    a.dtype = da.BF16
+    a.B, a.H, a.H_kv, a.N, a.d_qk, a.d_v = 1, 4, 2, 128, 64, 128
+    step = 1 << 24
+    a.q1, a.q2, a.k1, a.k2, a.v = FAKE, FAKE + step, FAKE + 2 * step, FAKE + 3 * step, FAKE + 4 * step
+    a.sq1 = a.sq2 = (ctypes.c_int64 * 3)(4 * 128 * 64, 128 * 64, 64)
+    a.sk1 = a.sk2 = (ctypes.c_int64 * 3)(2 * 128 * 64, 128 * 64, 64)
+    a.sv = (ctypes.c_int64 * 3)(2 * 128 * 128, 128 * 128, 128)
+    a.lambda_ = FAKE + 5 * step
+    a.depth, a.causal, a.window, a.scale, a.norm, a.eps = 3, 1, 0, 0.0, da.NORM_NONE, 1e-5
+    a.o1, a.o2, a.lse1, a.lse2 = FAKE + 6 * step, FAKE + 7 * step, FAKE + 8 * step, FAKE + 9 * step
+    a.dout = FAKE + 10 * step
+    a.sdo = (ctypes.c_int64 * 3)(4 * 128 * 128, 128 * 128, 128)
+    a.dq1, a.dq2, a.dk1, a.dk2, a.dv = (FAKE + (11 + i) * step for i in range(5))
+    a.dlambda = FAKE + 16 * step
+    a.dgamma = None
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_backward_workspace_sizes(lib):
+    a = _backward_args()
+    rows = 1 * 4 * 128
+    r256 = lambda x: -(-x // 256) * 256
+    want = r256(rows * 128 * 2) + 2 * r256(rows * 4) + r256(1 * 4 * 32 * 129 * 4)
+    assert lib.diffattn_backward_workspace_bytes(ctypes.byref(a)) == want
+    assert lib.diffattn_backward_workspace_bytes(ctypes.byref(_backward_args(dtype=da.F32))) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("dtype", da.F32, da.EUNSUPPORTED),
+    ("d_qk", 96, da.EUNSUPPORTED),
+    ("o1", None, da.EINVAL),
+    ("dout", None, da.EINVAL),
+    ("dq1", None, da.EINVAL),
+    ("dk2", None, da.EINVAL),                 # two key tensors need two key gradients
+    ("dq2", FAKE + 11 * (1 << 24), da.EINVAL),  # overlaps dq1
+    ("dv", FAKE, da.EINVAL),                  # overlaps q1
+    ("window", 4, None),                      # valid (checked below with causal = 0)
+])
+def test_backward_rejects(lib, field, value, code):
+    a = _backward_args(**{field: value})
+    if code is None:
+        a.causal = 0
+        code = da.EINVAL
+    rc = lib.diffattn_backward(ctypes.byref(a), FAKE + 20 * (1 << 24), 1 << 30, None)
+    assert rc == code
+    assert lib.diffattn_last_error().decode().startswith("diffattn_backward")
+
+
+def test_backward_rejects_small_workspace(lib):
+    a = _backward_args()
+    need = lib.diffattn_backward_workspace_bytes(ctypes.byref(a))
+    assert lib.diffattn_backward(ctypes.byref(a), FAKE + 20 * (1 << 24), need - 1, None) == da.EWORKSPACE
+
+
+def test_prefill_rejects_partial_statistics(lib):
+    a = _prefill_args(o1=FAKE + 6 * (1 << 24))
+    assert _rc(lib, a) == da.EINVAL

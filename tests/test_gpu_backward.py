@@ -1,0 +1,163 @@
+"""GPU parity of the backward pass (and of the statistics the forward stores
+for it) against the fp64 gradient oracle (oracle/backward.py), through the C ABI.
+
+Tolerance for gradients: each gradient tensor's relative Frobenius error
+<= 2e-2 and max |error| <= 5e-2 of its largest magnitude. The path rounds the
+output gradient after the norm and the score gradients to bf16 (8 significant
+bits, 2^-9 relative) before the products, as the forward rounds the
+probabilities; accumulation is fp32. dlambda and dgamma (sums over all rows):
+relative error <= 1e-2. The lambda-vector gradients (fp32 only): 1e-5 relative."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import PrefillCase, check, dev, say, to_dev
+from oracle import backward as bw
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL_FRO = 2e-2
+GRAD_MAX_REL = 5e-2
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+@pytest.fixture(scope="module")
+def da():
+    import differential_attention_amd as m
+    m.load_library()
+    return m
+
+
+def _case(form, N, causal, B=1, seed=0, H=None):
+    if form == "v1":
+        return W.prefill_v1(seed=seed, B=B, H=H or 2, N=N, causal=causal)
+    return W.prefill_v2(seed=seed, B=B, H=H or 4, H_kv=2, N=N, causal=causal)
+
+
+def _grad_check(got, ref, what, zero_scale=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    err = got - ref
+    if zero_scale is not None:
+        # a gradient that is zero by construction: bounded by rounding noise
+        # relative to the scale of the inputs that would otherwise feed it
+        mx = float(np.abs(got).max()) / zero_scale
+        say(f"  {what}: zero by construction, max|got| / scale {mx:.3e}")
+        assert mx <= 1e-3, (what, mx)
+        return
+    fro = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30))
+    mx = float(np.abs(err).max() / max(np.abs(ref).max(), 1e-30))
+    say(f"  {what}: rel-fro {fro:.3e} max/max|ref| {mx:.3e}")
+    assert fro <= GRAD_REL_FRO, (what, fro)
+    assert mx <= GRAD_MAX_REL, (what, mx)
+
+
+def _run(torch, da, p, window=0, seed=0):
+    c = PrefillCase(p)
+    stats = da.prefill_stats(c.q1, c.v)
+    c.run(window=window, stats=stats)
+    rng = np.random.default_rng(seed + 1000)
+    dout_bits = W.f32_to_bf16(rng.standard_normal((p.B, p.H, p.N, p.d_v)).astype(np.float32))
+    dout = to_dev(dout_bits, "bf16")
+    g = da.backward(c.q1, c.q2, c.k1, c.k2, c.v, c.lam, stats, dout, depth=p.depth, causal=p.causal,
+                    norm=p.norm, gamma=c.gamma, eps=p.eps, window=window)
+    k1 = p.f32("k1")
+    k2 = k1 if p.shared_k else p.f32("k2")
+    ref = bw.prefill_backward(p.f32("q1"), p.f32("q2"), k1, k2, p.f32("v"), c.lam64, W.bf16_to_f32(dout_bits),
+                              depth=p.depth, causal=p.causal, norm=p.norm, gamma=p.gamma, eps=p.eps,
+                              window=window)
+    return c, stats, g, ref
+
+
+@pytest.mark.parametrize("form", ["v1", "v2"])
+@pytest.mark.parametrize("N,causal,window", [(64, True, 0), (200, True, 0), (333, True, 0), (100, False, 0),
+                                             (257, True, 40), (200, True, 1)])
+def test_backward_parity(torch, da, form, N, causal, window):
+    p = _case(form, N, causal, seed=N + window)
+    say(f"backward {form} N {N} causal {causal} window {window}")
+    c, stats, g, ref = _run(torch, da, p, window=window, seed=N)
+    # the statistics the forward stored
+    check(stats[0].cpu().numpy(), ref["o1"], "bf16", "o1")
+    check(stats[1].cpu().numpy(), ref["o2"], "bf16", "o2")
+    for k in (2, 3):
+        d = np.abs(stats[k].cpu().numpy() - ref["lse1" if k == 2 else "lse2"]).max()
+        assert d <= 1e-2, ("lse", d)
+    # with a window of one key each softmax is the constant 1, so the score
+    # gradients, and with them dQ and dK, vanish identically (o_k = v_i)
+    zs = float(np.abs(ref["dv"]).max()) if window == 1 else None
+    for name in ("dq1", "dq2", "dv"):
+        _grad_check(g[name].cpu().numpy(), ref[name], name, zs if name != "dv" else None)
+    if p.shared_k:
+        _grad_check(g["dk1"].cpu().numpy(), ref["dk1"] + ref["dk2"], "dk (shared)", zs)
+    else:
+        _grad_check(g["dk1"].cpu().numpy(), ref["dk1"], "dk1", zs)
+        _grad_check(g["dk2"].cpu().numpy(), ref["dk2"], "dk2", zs)
+    dl = g["dlambda"].cpu().numpy()
+    assert np.all(np.abs(dl - ref["dlambda"]) <= 1e-2 * np.abs(ref["dlambda"]).max() + 1e-6), (dl, ref["dlambda"])
+    if p.norm:
+        dg = g["dgamma"].cpu().numpy()
+        assert np.linalg.norm(dg - ref["dgamma"]) <= 1e-2 * np.linalg.norm(ref["dgamma"])
+
+
+def test_backward_gqa_groups(torch, da):
+    # 8 heads over 2 KV heads (4 heads per KV head accumulate into one dK, dV)
+    p = W.prefill_v2(seed=5, B=2, H=8, H_kv=2, N=150)
+    say("backward V2 8/2 heads, B 2, N 150")
+    _, _, g, ref = _run(torch, da, p, seed=5)
+    _grad_check(g["dk1"].cpu().numpy(), ref["dk1"] + ref["dk2"], "dk (shared, GQA)")
+    _grad_check(g["dv"].cpu().numpy(), ref["dv"], "dv (GQA)")
+    _grad_check(g["dq2"].cpu().numpy(), ref["dq2"], "dq2 (GQA)")
+
+
+def test_backward_is_deterministic(torch, da):
+    p = _case("v1", 300, True, seed=9)
+    c = PrefillCase(p)
+    stats = da.prefill_stats(c.q1, c.v)
+    c.run(stats=stats)
+    dout = to_dev(W.f32_to_bf16(np.ones((p.B, p.H, p.N, p.d_v), np.float32)), "bf16")
+    g1 = da.backward(c.q1, c.q2, c.k1, c.k2, c.v, c.lam, stats, dout, depth=p.depth, norm=True, gamma=c.gamma)
+    g2 = da.backward(c.q1, c.q2, c.k1, c.k2, c.v, c.lam, stats, dout, depth=p.depth, norm=True, gamma=c.gamma)
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g1[k], g2[k]), k
+
+
+def test_lambda_backward(torch, da):
+    rng = np.random.default_rng(3)
+    H, dl = 5, 64
+    vec = [(rng.standard_normal((H, dl)) * 0.1).astype(np.float32) for _ in range(4)]
+    dlam = rng.standard_normal(H).astype(np.float32)
+    got = da.lambda_backward(*(torch.from_numpy(x).to(dev()) for x in vec), torch.from_numpy(dlam).to(dev()))
+    ref = bw.lambda_backward(*vec, dlam)
+    for k in ref:
+        np.testing.assert_allclose(got[k].cpu().numpy(), ref[k], rtol=1e-5, atol=1e-7)
+
+
+def test_backward_prefill_v1_shape_sampled_heads(torch, da):
+    # the prefill_v1 shape (B 2, H 16, N 4096, V1, RMS): gradients of two heads
+    # compared in full (the oracle materialises their 4096 x 4096 maps)
+    p = W.prefill_v1()
+    c = PrefillCase(p)
+    stats = da.prefill_stats(c.q1, c.v)
+    c.run(stats=stats)
+    rng = np.random.default_rng(77)
+    dout_bits = W.f32_to_bf16(rng.standard_normal((p.B, p.H, p.N, p.d_v)).astype(np.float32))
+    g = da.backward(c.q1, c.q2, c.k1, c.k2, c.v, c.lam, stats, to_dev(dout_bits, "bf16"), depth=p.depth,
+                    norm=True, gamma=c.gamma, eps=p.eps)
+    for b, h in ((0, 3), (1, 14)):
+        say(f"backward prefill_v1 shape, head (b {b}, h {h})")
+        sl = lambda x: x[b:b + 1, h:h + 1]
+        ref = bw.prefill_backward(sl(p.f32("q1")), sl(p.f32("q2")), sl(p.f32("k1")), sl(p.f32("k2")),
+                                  sl(p.f32("v")), c.lam64[h:h + 1], sl(W.bf16_to_f32(dout_bits)), depth=p.depth,
+                                  causal=True, norm=True, gamma=p.gamma[h:h + 1], eps=p.eps)
+        for name in ("dq1", "dq2", "dk1", "dk2", "dv"):
+            _grad_check(sl(g[name].cpu().numpy()), ref[name], f"{name} (b {b}, h {h})")
