@@ -51,6 +51,15 @@ def prefill_flops(B, H, N, dqk, dv, window=0):
     return B * H * pairs * 2.0 * (2 * dqk + 2 * dv)
 
 
+def backward_flops(B, H, N, dqk, dv, window=0):
+    """Algorithmic FLOPs of the prefill's backward per visible (query, key)
+    pair: both branches' scores recomputed (2 x 2 d_qk), the output-gradient
+    product dy V^T shared by the branches (2 d_v), dV from the combined weight
+    (2 d_v), dQ and dK of both branches (4 x 2 d_qk): 12 d_qk + 4 d_v."""
+    pairs = N * N / 2.0 if not window or window >= N else window * window / 2.0 + (N - window) * window
+    return B * H * pairs * (12 * dqk + 4 * dv)
+
+
 def decode_bytes(d):
     """Algorithmic HBM bytes of one decode call: every visible token's keys
     (one cache, or one per branch) and values once, the queries, the output,
@@ -67,11 +76,13 @@ def decode_bytes(d):
 
 # sources of the kernels each workload runs (their hash keys the stored counters)
 KERNEL_SOURCES = {
-    "prefill_v1": ["prefill_bf16.hip", "common.hpp"],
-    "prefill_v2": ["prefill_bf16.hip", "common.hpp"],
-    "longctx_v1": ["prefill_bf16.hip", "common.hpp"],
+    "prefill_v1": ["prefill_bf16.hip", "tiles.hpp", "common.hpp"],
+    "prefill_v2": ["prefill_bf16.hip", "tiles.hpp", "common.hpp"],
+    "longctx_v1": ["prefill_bf16.hip", "tiles.hpp", "common.hpp"],
     "decode_v2": ["decode.hip", "common.hpp"],
     "decode_v1": ["decode.hip", "common.hpp"],
+    "backward_v1": ["backward.hip", "tiles.hpp", "common.hpp"],
+    "backward_v2": ["backward.hip", "tiles.hpp", "common.hpp"],
 }
 
 
@@ -164,6 +175,34 @@ def single_workload(args, torch, da, W, dev):
         else:
             desc = ("decode_v1: V1 paged decode, 64 seqs, ctx U{8192..32768}, 8 KV / 32 heads, d_qk 64 "
                     "(K1, K2 caches), d_v 128, page 64, RMS norm")
+    elif name in ("backward_v1", "backward_v2"):
+        p = W.prefill_v1() if name == "backward_v1" else W.prefill_v2()
+        if p.q_full is not None:
+            qf = to_dev(p.q_full)
+            q1, q2 = qf[:, 0::2], qf[:, 1::2]
+        else:
+            q1, q2 = to_dev(p.q1), to_dev(p.q2)
+        k1 = to_dev(p.k1)
+        k2 = k1 if p.shared_k else to_dev(p.k2)
+        v = to_dev(p.v)
+        gamma = torch.from_numpy(p.gamma).to(dev) if p.norm else None
+        lam = da.lambda_(*(torch.from_numpy(x).to(dev) for x in (p.lam_q1, p.lam_k1, p.lam_q2, p.lam_k2)), p.depth)
+        stats = da.prefill_stats(q1, v)
+        win = args.window
+        da.prefill(q1, q2, k1, k2, v, lam, depth=p.depth, causal=p.causal, norm=p.norm, gamma=gamma, eps=p.eps,
+                   window=win, stats=stats)
+        dout = torch.randn((p.B, p.H, p.N, p.d_v), generator=torch.Generator().manual_seed(7)).to(
+            dev, torch.bfloat16)
+        kw = dict(depth=p.depth, causal=p.causal, norm=p.norm, gamma=gamma, eps=p.eps, window=win)
+        # the gradient tensors and workspace come from torch's caching allocator
+        # (no device allocation after the first call)
+        call = lambda: da.backward(q1, q2, k1, k2, v, lam, stats, dout, **kw)
+        work = backward_flops(p.B, p.H, p.N, p.d_qk, p.d_v, win)
+        unit, metric, bound = "TFLOP/s", "prefill backward TFLOP/s (algorithmic)", "mfma"
+        desc = (f"{name}: gradients of the {'prefill_v1' if name == 'backward_v1' else 'prefill_v2'} "
+                f"prefill (B {p.B}, H {p.H}, H_kv {p.H_kv}, N {p.N}, d_qk {p.d_qk}, d_v {p.d_v}), fp32 gradients")
+        if win:
+            desc += f", causal window {win}"
     else:
         p = getattr(W, name)()
         dt = p.dtype
@@ -220,13 +259,13 @@ def main():
                     help="profiling aid: run only one part of the step")
     ap.add_argument("--workload", default="step",
                     choices=["step", "prefill_v1", "prefill_v2", "longctx_v1", "tiny_v1", "decode_v2",
-                             "decode_v1", "copy"],
+                             "decode_v1", "backward_v1", "backward_v2", "copy"],
                     help="step: the whole path (default); otherwise time one workload alone "
                          "(copy: a plain device copy of 4 GiB, for calibrating HBM byte counters)")
     ap.add_argument("--window", type=int, default=0,
                     help="causal sliding window for a single prefill workload (0 = none)")
     args = ap.parse_args()
-    if args.window and args.workload in ("step", "copy", "decode_v2", "decode_v1"):
+    if args.window and args.workload in ("step", "copy", "decode_v2", "decode_v1", "tiny_v1"):
         ap.error("--window applies to a single prefill workload")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "

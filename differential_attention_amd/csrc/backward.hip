@@ -18,8 +18,8 @@
 //
 // Kernels:
 //  bwd_prep_kernel      one wave per row: dy (stored bf16, the MFMA operand),
-//                       rowsum(dy o_k) from the rounded dy, and per block of 4
-//                       rows the partial sums of dlambda and dgamma
+//                       rowsum(dy o_k) from the rounded dy, and per block of
+//                       64 rows the partial sums of dlambda and dgamma
 //  bwd_dq_kernel        query-major, like the forward: a work-group owns 128
 //                       rows of one head, 8 waves = 4 row groups x 2 branches;
 //                       per 32-key sub-block S^T = K Q^T, G^T = V dy^T,
@@ -60,15 +60,20 @@ struct BwdParams {
 // ---------------------------------------------------------------- prep
 
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+    // a block of kBwdPrepRows rows of one (batch, head): each wave takes every
+    // 4th row; the block's dlambda and dgamma sums go to one partial record
     __shared__ float red[4][kDV + 1];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int i = blk * kBwdPrepRows + wave;
     const int c0 = lane, c1 = lane + 64;
+    const float lam = p.lambda[h];
+    const float c = p.one_minus_init;
+    const float gm0 = p.norm ? c * p.gamma[(int64_t)h * kDV + c0] : 0.0f;
+    const float gm1 = p.norm ? c * p.gamma[(int64_t)h * kDV + c1] : 0.0f;
     float dl = 0.0f, pg0 = 0.0f, pg1 = 0.0f;
-    if (i < p.N) {
+    const int iend = min(p.N, (blk + 1) * kBwdPrepRows);
+    for (int i = blk * kBwdPrepRows + wave; i < iend; i += 4) {
         const int64_t rowid = ((int64_t)b * p.H + h) * p.N + i;
-        const float lam = p.lambda[h];
         const float a0 = p.o1[rowid * kDV + c0], a1 = p.o1[rowid * kDV + c1];
         const float e0 = p.o2[rowid * kDV + c0], e1 = p.o2[rowid * kDV + c1];
         const __bf16 *dz = p.dout + b * p.sdo[0] + h * p.sdo[1] + (int64_t)i * p.sdo[2];
@@ -82,16 +87,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
         float d0 = z0, d1 = z1;
         if (p.norm) {
             const float r = 1.0f / sqrtf(wave_sum(y0 * y0 + y1 * y1) * (1.0f / kDV) + p.eps);
-            const float c = p.one_minus_init;
-            const float g0 = c * p.gamma[(int64_t)h * kDV + c0] * z0;
-            const float g1 = c * p.gamma[(int64_t)h * kDV + c1] * z1;
+            const float g0 = gm0 * z0, g1 = gm1 * z1;
             const float k3 = r * r * r * (1.0f / kDV) * wave_sum(g0 * y0 + g1 * y1);
             d0 = r * g0 - y0 * k3;
             d1 = r * g1 - y1 * k3;
-            pg0 = z0 * y0 * r * c;
-            pg1 = z1 * y1 * r * c;
+            pg0 += z0 * y0 * r * c;
+            pg1 += z1 * y1 * r * c;
         }
-        dl = -wave_sum(d0 * e0 + d1 * e1);
+        dl -= wave_sum(d0 * e0 + d1 * e1);
         const __bf16 b0 = (__bf16)d0, b1 = (__bf16)d1;
         p.dy[rowid * kDV + c0] = b0;
         p.dy[rowid * kDV + c1] = b1;
@@ -109,24 +112,36 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     if (lane == 0) red[wave][kDV] = dl;
     __syncthreads();
     float *pp = p.part + (((int64_t)b * p.H + h) * p.prep_nblk + blk) * (kDV + 1);
-    for (int c = threadIdx.x; c <= kDV; c += 256) {
-        const float s = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
-        pp[c == kDV ? 0 : 1 + c] = s;
+    for (int k = threadIdx.x; k <= kDV; k += 256) {
+        const float s = (red[0][k] + red[1][k]) + (red[2][k] + red[3][k]);
+        pp[k == kDV ? 0 : 1 + k] = s;
     }
 }
 
-__global__ __launch_bounds__(128) void bwd_finalize_kernel(BwdParams p) {
-    const int h = blockIdx.x, c = threadIdx.x;
-    float sg = 0.0f, sl = 0.0f;
-    for (int b = 0; b < p.B; ++b) {
-        const float *pp = p.part + ((int64_t)b * p.H + h) * p.prep_nblk * (kDV + 1);
-        for (int k = 0; k < p.prep_nblk; ++k) {
-            sg += pp[(int64_t)k * (kDV + 1) + 1 + c];
-            sl += pp[(int64_t)k * (kDV + 1)];
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
+    // per head: the partial records summed in a fixed order (deterministic);
+    // thread t < 129 owns value t of every record (t = 0: dlambda, else
+    // dgamma[t - 1]) and keeps 8 independent running sums
+    const int h = blockIdx.x, t = threadIdx.x;
+    if (t > kDV) return;
+    const int64_t n = (int64_t)p.B * p.prep_nblk;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int64_t k = 0;
+    for (; k + 8 <= n; k += 8)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t r = k + e, bb = r / p.prep_nblk, kb = r - bb * p.prep_nblk;
+            acc[e] += p.part[(((int64_t)bb * p.H + h) * p.prep_nblk + kb) * (kDV + 1) + t];
         }
+    for (; k < n; ++k) {
+        const int64_t bb = k / p.prep_nblk, kb = k - bb * p.prep_nblk;
+        acc[0] += p.part[(((int64_t)bb * p.H + h) * p.prep_nblk + kb) * (kDV + 1) + t];
     }
-    if (p.norm) p.dgamma[(int64_t)h * kDV + c] = sg;
-    if (c == 0) p.dlambda[h] = sl;
+    const float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    if (t == 0)
+        p.dlambda[h] = s;
+    else if (p.norm)
+        p.dgamma[(int64_t)h * kDV + t - 1] = s;
 }
 
 // ---------------------------------------------------------------- dQ
@@ -619,7 +634,7 @@ hipError_t launch_backward_bf16(const diffattn_backward_args &a, const BackwardP
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(p.prep_nblk, a.H, a.B), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_finalize_kernel, dim3(a.H), dim3(kDV), 0, stream, p);
+    hipLaunchKernelGGL(bwd_finalize_kernel, dim3(a.H), dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.d_qk == 64) return plan.shared_k ? launch_w<64, true>(p, stream) : launch_w<64, false>(p, stream);

@@ -45,7 +45,7 @@ struct PrefillPlan {
 // (bf16, one d_v row per query row), two per-row reductions (rowsum of the
 // output gradient times each branch's normalised output) and, per block of
 // kBwdPrepRows rows, the partial sums of dlambda and dgamma.
-constexpr int kBwdPrepRows = 4;
+constexpr int kBwdPrepRows = 64;
 
 struct BackwardPlan {
     bool shared_k = false;
