@@ -25,7 +25,19 @@ LIB_PATH = os.path.join(_PKG, "libdiffattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
-NORM_NONE, NORM_RMS = 0, 1
+NORM_NONE, NORM_RMS, NORM_GROUP = 0, 1, 2
+
+
+def _norm_code(norm) -> int:
+    """norm: False/None (V2, no norm), True or "rms" (V1 RMSNorm), "group"
+    (V1 GroupNorm per head, mean subtracted)."""
+    if norm in (False, None, 0):
+        return NORM_NONE
+    if norm in (True, "rms", 1):
+        return NORM_RMS
+    if norm in ("group", 2):
+        return NORM_GROUP
+    raise ValueError(f"unknown norm {norm!r}")
 
 _c_int64_3 = ctypes.c_int64 * 3
 _c_int64_2 = ctypes.c_int64 * 2
@@ -245,7 +257,7 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool = True, norm: bo
                 raise ValueError(f"stats tensors must be contiguous fp32 of shapes {shape}")
         a.o1, a.o2, a.lse1, a.lse2 = (_ptr(t) for t in stats)
     a.scale = float(scale)
-    a.norm = NORM_RMS if norm else NORM_NONE
+    a.norm = _norm_code(norm)
     a.gamma = _ptr(gamma) if norm else None
     a.eps = float(eps)
     a.out = _ptr(out)
@@ -290,7 +302,7 @@ def backward(q1, q2, k1, k2, v, lam, stats, dout, *, depth: int, causal: bool = 
     a.sv = _c_int64_3(*_strides3(v))
     a.lambda_ = _ptr(lam)
     a.depth, a.causal, a.window, a.scale = int(depth), int(bool(causal)), int(window), float(scale)
-    a.norm = NORM_RMS if norm else NORM_NONE
+    a.norm = _norm_code(norm)
     a.gamma = _ptr(gamma) if norm else None
     a.eps = float(eps)
     for t in stats:
@@ -347,7 +359,7 @@ def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm
     a.lambda_ = _ptr(lam)
     a.depth = int(depth)
     a.scale = float(scale)
-    a.norm = NORM_RMS if norm else NORM_NONE
+    a.norm = _norm_code(norm)
     a.gamma = _ptr(gamma) if norm else None
     a.eps = float(eps)
     a.out = _ptr(out) if out is not None else None

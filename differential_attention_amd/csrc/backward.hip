@@ -86,9 +86,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
         }
         float d0 = z0, d1 = z1;
         if (p.norm) {
+            // RMS: z = y r gamma c; GroupNorm: z = u r gamma c with u = y - mean(y)
+            // (r from the mean square of y, resp. u); with gd = c gamma dz:
+            //   RMS:   dy = r gd - y r^3 mean(gd y)
+            //   group: dy = r (gd - mean(gd)) - u r^3 mean(gd u)
+            if (p.norm == 2) {
+                const float mu = wave_sum(y0 + y1) * (1.0f / kDV);
+                y0 -= mu;
+                y1 -= mu;
+            }
             const float r = 1.0f / sqrtf(wave_sum(y0 * y0 + y1 * y1) * (1.0f / kDV) + p.eps);
-            const float g0 = gm0 * z0, g1 = gm1 * z1;
+            float g0 = gm0 * z0, g1 = gm1 * z1;
             const float k3 = r * r * r * (1.0f / kDV) * wave_sum(g0 * y0 + g1 * y1);
+            if (p.norm == 2) {
+                const float gmean = wave_sum(g0 + g1) * (1.0f / kDV);
+                g0 -= gmean;
+                g1 -= gmean;
+            }
             d0 = r * g0 - y0 * k3;
             d1 = r * g1 - y1 * k3;
             pg0 += z0 * y0 * r * c;
@@ -622,7 +636,7 @@ hipError_t launch_backward_bf16(const diffattn_backward_args &a, const BackwardP
     p.N = a.N;
     p.causal = a.causal;
     p.window = a.window;
-    p.norm = a.norm == DIFFATTN_NORM_RMS;
+    p.norm = a.norm;  // 0 none, 1 RMS, 2 GroupNorm
     p.prep_nblk = (a.N + kBwdPrepRows - 1) / kBwdPrepRows;
     p.row_blocks = (a.N + kBM - 1) / kBM;
     p.key_blocks = (a.N + kKB - 1) / kKB;

@@ -384,7 +384,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 }
 
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
-    __shared__ float red[2];
+    __shared__ float red[4];
     const int h = blockIdx.x, b = blockIdx.y, dv = threadIdx.x;
     const int g = h / p.group, j = h - g * p.group;
     const int L = p.ctx_len[b];
@@ -428,6 +428,12 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
         y = ob[0] - p.lambda[h] * ob[1];
     }
     if (p.norm) {
+        if (p.norm == 2) {  // GroupNorm per head: subtract the channel mean first
+            const float sm = wave_sum(y);
+            if ((dv & 63) == 0) red[2 + (dv >> 6)] = sm;
+            __syncthreads();
+            y -= (red[2] + red[3]) * (1.0f / kDV);
+        }
         float ss = wave_sum(y * y);
         if ((dv & 63) == 0) red[dv >> 6] = ss;
         __syncthreads();
@@ -493,7 +499,7 @@ hipError_t launch_decode_bf16(const diffattn_decode_args &a, const DecodePlan &p
     p.num_wgs = plan.target_pages > 0
                     ? plan.max_wgs
                     : std::min(plan.max_wgs, kRounds * (d64 ? resident_split_wgs<64>() : resident_split_wgs<128>()));
-    p.norm = a.norm == DIFFATTN_NORM_RMS;
+    p.norm = a.norm;  // 0 none, 1 RMS, 2 GroupNorm
     p.window = a.window;
     p.sc_log2 = scale * kLog2e;
     p.eps = a.eps;

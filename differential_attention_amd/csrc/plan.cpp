@@ -103,11 +103,11 @@ int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string
     const int nstats = (a->o1 != nullptr) + (a->o2 != nullptr) + (a->lse1 != nullptr) + (a->lse2 != nullptr);
     if (nstats != 0 && nstats != 4)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: set all of o1, o2, lse1, lse2 or none");
-    if (a->norm != DIFFATTN_NORM_NONE && a->norm != DIFFATTN_NORM_RMS)
+    if (a->norm != DIFFATTN_NORM_NONE && a->norm != DIFFATTN_NORM_RMS && a->norm != DIFFATTN_NORM_GROUP)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: unknown norm");
     if (!(a->scale >= 0.0f) || isinf(a->scale))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: scale must be finite and >= 0");
-    if (a->norm == DIFFATTN_NORM_RMS && !(a->eps > 0.0f && !isinf(a->eps)))
+    if (a->norm != DIFFATTN_NORM_NONE && !(a->eps > 0.0f && !isinf(a->eps)))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: eps must be finite and > 0");
 
     if (a->dtype == DIFFATTN_BF16) {
@@ -127,8 +127,8 @@ int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string
     }
     if (!a->q1 || !a->q2 || !a->k1 || !a->k2 || !a->v || !a->lambda || !a->out)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: null tensor pointer");
-    if (a->norm == DIFFATTN_NORM_RMS && !a->gamma)
-        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: RMS norm needs gamma");
+    if (a->norm != DIFFATTN_NORM_NONE && !a->gamma)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: a norm needs gamma");
 
     const size_t elem = a->dtype == DIFFATTN_BF16 ? 2 : 4;
     const size_t align = a->dtype == DIFFATTN_BF16 ? 16 : 4;
@@ -158,14 +158,14 @@ int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string
         if (i == 5 && !non_overlapping(dims))
             return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: out has overlapping elements");
     }
-    if (!aligned(a->lambda, 4) || (a->gamma && a->norm == DIFFATTN_NORM_RMS && !aligned(a->gamma, 4)))
+    if (!aligned(a->lambda, 4) || (a->gamma && a->norm != DIFFATTN_NORM_NONE && !aligned(a->gamma, 4)))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: lambda/gamma misaligned");
     Extent lam{(uintptr_t)a->lambda, (uintptr_t)a->lambda + (uintptr_t)a->H * 4};
     for (int i = 0; i < 5; ++i)
         if (overlaps(ext[5], ext[i]))
             return fail(msg, DIFFATTN_EINVAL, std::string("diffattn_prefill: out overlaps ") + ts[i].name);
     if (overlaps(ext[5], lam)) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: out overlaps lambda");
-    if (a->norm == DIFFATTN_NORM_RMS) {
+    if (a->norm != DIFFATTN_NORM_NONE) {
         Extent g{(uintptr_t)a->gamma, (uintptr_t)a->gamma + (uintptr_t)a->H * a->d_v * 4};
         if (overlaps(ext[5], g)) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: out overlaps gamma");
     }
@@ -201,11 +201,11 @@ int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::str
     if (a->d_qk < 1 || a->d_v < 1 || a->page_size < 1 || a->max_pages < 1 || a->num_pages < 1)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: sizes must be >= 1");
     if (a->depth < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: depth must be >= 1");
-    if (a->norm != DIFFATTN_NORM_NONE && a->norm != DIFFATTN_NORM_RMS)
+    if (a->norm != DIFFATTN_NORM_NONE && a->norm != DIFFATTN_NORM_RMS && a->norm != DIFFATTN_NORM_GROUP)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: unknown norm");
     if (!(a->scale >= 0.0f) || isinf(a->scale))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: scale must be finite and >= 0");
-    if (a->norm == DIFFATTN_NORM_RMS && !(a->eps > 0.0f && !isinf(a->eps)))
+    if (a->norm != DIFFATTN_NORM_NONE && !(a->eps > 0.0f && !isinf(a->eps)))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: eps must be finite and > 0");
     if (a->window < 0) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: window must be >= 0");
     if (a->split_pages < 0 || a->split_pages > kDecodeMaxTarget)
@@ -248,8 +248,8 @@ int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *m
     if (!a->q1 || !a->q2 || !a->k1_cache || !a->k2_cache || !a->v_cache || !a->page_table || !a->ctx_len ||
         !a->lambda || !a->out)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: null pointer");
-    if (a->norm == DIFFATTN_NORM_RMS && !a->gamma)
-        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: RMS norm needs gamma");
+    if (a->norm != DIFFATTN_NORM_NONE && !a->gamma)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: a norm needs gamma");
     const int64_t strides[6] = {a->sq1[0], a->sq1[1], a->sq2[0], a->sq2[1], a->so[0], a->so[1]};
     for (int64_t s : strides)
         if (s < 0 || s % 8 != 0)
@@ -381,8 +381,8 @@ int check_backward(const diffattn_backward_args *a, BackwardPlan *plan, std::str
     } else if (!a->dk2 || a->dk2 == a->dk1) {
         return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: two key tensors need two key gradients");
     }
-    if (a->norm == DIFFATTN_NORM_RMS && !a->dgamma)
-        return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: RMS norm needs dgamma");
+    if (a->norm != DIFFATTN_NORM_NONE && !a->dgamma)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: a norm needs dgamma");
     const void *al16[] = {a->o1, a->o2, a->dq1, a->dq2, a->dk1, a->dk2 ? a->dk2 : a->dk1, a->dv};
     for (const void *p : al16)
         if (!aligned(p, 16)) return fail(msg, DIFFATTN_EINVAL, "diffattn_backward: fp32 tensor not 16-byte aligned");
@@ -398,10 +398,10 @@ int check_backward(const diffattn_backward_args *a, BackwardPlan *plan, std::str
                                 E(a->dk1, kvrows * a->d_qk * 4), E(a->dv, kvrows * a->d_v * 4),
                                 E(a->dlambda, (uintptr_t)a->H * 4)};
     if (!plan->shared_k) outs.push_back(E(a->dk2, kvrows * a->d_qk * 4));
-    if (a->norm == DIFFATTN_NORM_RMS) outs.push_back(E(a->dgamma, (uintptr_t)a->H * a->d_v * 4));
+    if (a->norm != DIFFATTN_NORM_NONE) outs.push_back(E(a->dgamma, (uintptr_t)a->H * a->d_v * 4));
     std::vector<Extent> ins = {E(a->o1, rows * a->d_v * 4), E(a->o2, rows * a->d_v * 4), E(a->lse1, rows * 4),
                                E(a->lse2, rows * 4), E(a->lambda, (uintptr_t)a->H * 4)};
-    if (a->norm == DIFFATTN_NORM_RMS && a->gamma) ins.push_back(E(a->gamma, (uintptr_t)a->H * a->d_v * 4));
+    if (a->norm != DIFFATTN_NORM_NONE && a->gamma) ins.push_back(E(a->gamma, (uintptr_t)a->H * a->d_v * 4));
     // the strided bf16 inputs, by their extents
     struct T {
         const void *p;

@@ -80,6 +80,7 @@ struct Bf16Params {
     __bf16 *out;
     float *o1, *o2, *lse1, *lse2;  // optional statistics for the backward pass (all or none)
     int B, H, H_kv, group, N, causal, window, row_blocks, xcd_units;
+    int group_norm;  // the norm subtracts the channel mean first (GroupNorm per head)
     float sc_log2;  // scale * log2(e)
     float eps, one_minus_init;
 };
@@ -406,6 +407,18 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         }
     }
     if constexpr (NORM) {
+        if (p.group_norm) {
+            float sm = 0.0f;
+#pragma unroll
+            for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sm += y[dc][r];
+            const float mu = halves_sum(sm) * (1.0f / kDV);
+#pragma unroll
+            for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) y[dc][r] -= mu;
+        }
         float ss = 0.0f;
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc)
@@ -485,7 +498,8 @@ hipError_t launch_prefill_bf16(const diffattn_prefill_args &a, float scale, floa
     const int64_t blocks = (int64_t)a.B * a.H * p.row_blocks;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool shared = a.k1 == a.k2 && a.sk1[0] == a.sk2[0] && a.sk1[1] == a.sk2[1] && a.sk1[2] == a.sk2[2];
-    const bool norm = a.norm == DIFFATTN_NORM_RMS;
+    const bool norm = a.norm != DIFFATTN_NORM_NONE;
+    p.group_norm = a.norm == DIFFATTN_NORM_GROUP;
     const int nb = (int)blocks;
     if (a.d_qk == 64) {
         if (shared) return norm ? launch_t<64, true, true>(p, nb, stream) : launch_t<64, true, false>(p, nb, stream);

@@ -122,6 +122,11 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillF32Params p) {
         yb = c1 < p.d_v ? o1b * r1 - o2b * r2 : 0.0f;
     }
     if (p.norm) {
+        if (p.norm == 2) {  // GroupNorm per head: subtract the channel mean first
+            const float mu = wave_sum((c0 < p.d_v ? ya : 0.0f) + (c1 < p.d_v ? yb : 0.0f)) / (float)p.d_v;
+            if (c0 < p.d_v) ya -= mu;
+            if (c1 < p.d_v) yb -= mu;
+        }
         const float ss = wave_sum(ya * ya + yb * yb);
         const float rs = p.one_minus_init / sqrtf(ss / (float)p.d_v + p.eps);
         if (c0 < p.d_v) ya *= rs * p.gamma[(int64_t)h * p.d_v + c0];
@@ -162,7 +167,7 @@ hipError_t launch_prefill_f32(const diffattn_prefill_args &a, float scale, float
     p.d_v = a.d_v;
     p.causal = a.causal;
     p.window = a.window;
-    p.norm = a.norm == DIFFATTN_NORM_RMS;
+    p.norm = a.norm;  // 0 none, 1 RMS, 2 GroupNorm
     p.scale = scale;
     p.eps = a.eps;
     p.one_minus_init = 1.0f - lambda_init;

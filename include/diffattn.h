@@ -53,7 +53,12 @@ enum {
 };
 
 enum { DIFFATTN_BF16 = 0, DIFFATTN_F32 = 1 };
-enum { DIFFATTN_NORM_NONE = 0 /* V2 */, DIFFATTN_NORM_RMS = 1 /* V1 */ };
+enum {
+    DIFFATTN_NORM_NONE = 0,  /* V2 */
+    DIFFATTN_NORM_RMS = 1,   /* V1: y / sqrt(mean(y^2) + eps) * gamma * (1 - lambda_init) */
+    DIFFATTN_NORM_GROUP = 2  /* V1 variant, GroupNorm with one group per head:
+                                (y - mean y) / sqrt(var(y) + eps) * gamma * (1 - lambda_init) */
+};
 
 /*
  * Prefill arguments. Shapes:
@@ -79,8 +84,8 @@ typedef struct {
     int depth;           /* >= 1; lambda_init(depth) feeds the V1 (1 - lambda_init) scale */
     int causal;          /* 0 or 1 */
     float scale;         /* score scale; 0 selects 1/sqrt(d_qk) */
-    int norm;            /* DIFFATTN_NORM_NONE or DIFFATTN_NORM_RMS */
-    const float *gamma;  /* RMS: [H, d_v] fp32 device gain; NONE: ignored (may be NULL) */
+    int norm;            /* DIFFATTN_NORM_NONE, _RMS or _GROUP */
+    const float *gamma;  /* RMS / GROUP: [H, d_v] fp32 device gain; NONE: ignored (may be NULL) */
     float eps;           /* RMSNorm epsilon, > 0 */
     void *out;
     int64_t so[3];
@@ -192,7 +197,7 @@ int diffattn_decode(const diffattn_decode_args *a, void *workspace, size_t ws_by
  *             NULL or equal to dk1
  *   dv        [B, H_kv, N, d_v]
  *   dlambda   [H]           (feed diffattn_lambda_backward for the four vectors)
- *   dgamma    [H, d_v]      (RMS norm only; may be NULL otherwise)
+ *   dgamma    [H, d_v]      (with a norm; may be NULL otherwise)
  * The workspace (diffattn_backward_workspace_bytes) holds the output gradient
  * after the norm in bf16 and per-row reductions; 256-byte aligned.
  */

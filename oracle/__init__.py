@@ -76,6 +76,17 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _norm_code(norm) -> int:
+    """norm: False/None (V2), True or "rms" (V1 RMSNorm), "group" (GroupNorm per head)."""
+    if norm in (False, None, 0):
+        return 0
+    if norm in (True, "rms", 1):
+        return 1
+    if norm in ("group", 2):
+        return 2
+    raise ValueError(f"unknown norm {norm!r}")
+
+
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
@@ -110,7 +121,7 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool, norm: bool,
     assert q2.shape == q1.shape and k1.shape == (B, Hkv, N, dqk) and k2.shape == k1.shape
     assert v.shape == (B, Hkv, N, dv)
     lam = np.ascontiguousarray(lam, dtype=np.float64).reshape(H)
-    g = _f32(gamma).reshape(H, dv) if norm else None
+    g = _f32(gamma).reshape(H, dv) if _norm_code(norm) else None
     if scale is None:
         scale = 1.0 / np.sqrt(dqk)
     if rows is None:
@@ -124,7 +135,7 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool, norm: bool,
         rp = _ptr(rows)
     rc = _load().oracle_prefill(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), B, H, Hkv, N, dqk, dv,
                                 _ptr(lam), int(depth), int(bool(causal)), int(window), float(scale),
-                                int(bool(norm)),
+                                _norm_code(norm),
                                 _ptr(g), float(eps), rp, nrows, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_prefill: invalid argument")
@@ -145,13 +156,13 @@ def decode(q1, q2, k1_cache, k2_cache, v_cache, page_table, ctx_len, lam, *, dep
     ctx = np.ascontiguousarray(ctx_len, dtype=np.int32)
     max_pages = table.shape[1]
     lam = np.ascontiguousarray(lam, dtype=np.float64).reshape(H)
-    g = _f32(gamma).reshape(H, dv) if norm else None
+    g = _f32(gamma).reshape(H, dv) if _norm_code(norm) else None
     if scale is None:
         scale = 1.0 / np.sqrt(dqk)
     out = np.empty((B, H, dv), np.float64)
     rc = _load().oracle_decode(_ptr(q1), _ptr(q2), _ptr(kc1), _ptr(kc2), _ptr(vc), B, H, Hkv, dqk, dv,
                                page, max_pages, P, _ptr(table), _ptr(ctx), _ptr(lam), int(depth),
-                               int(window), float(scale), int(bool(norm)), _ptr(g), float(eps), _ptr(out))
+                               int(window), float(scale), _norm_code(norm), _ptr(g), float(eps), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_decode: invalid argument or page id")
     return out

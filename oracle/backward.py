@@ -17,6 +17,7 @@ medium shapes only):
     O_k = A_k V
     y   = O_1 - lambda O_2
     V1: z = y * r * gamma * c,  r = 1/sqrt(mean(y^2) + eps), c = 1 - lambda_init
+        (GroupNorm variant: y - mean(y) in place of y, its variance in r)
   backward, given dz:
     V1: dgamma += sum_rows dz * y * r * c
         dy = c r (gamma dz) - y r^3 / d_v * sum_c(c gamma dz y)
@@ -103,7 +104,16 @@ def prefill_backward(q1, q2, k1, k2, v, lam, dout, *, depth: int, causal: bool, 
             out["lse1"][b, h], out["lse2"][b, h] = lse1, lse2
 
             dz = dout[b, h]
-            if norm:
+            if norm == "group":
+                # z = (y - mean y) r gamma c with r = 1/sqrt(var + eps):
+                # with u = y - mean y and gd = c gamma dz,
+                # dy = r (gd - mean(gd)) - u r^3 mean(gd u)
+                u = y - y.mean(axis=1, keepdims=True)
+                r = 1.0 / np.sqrt((u * u).mean(axis=1, keepdims=True) + eps)
+                out["dgamma"][h] += (dz * u * r * c).sum(axis=0)
+                gd = c * g[h][None, :] * dz
+                dy = r * (gd - gd.mean(axis=1, keepdims=True)) - u * r ** 3 * (gd * u).mean(axis=1, keepdims=True)
+            elif norm:
                 r = 1.0 / np.sqrt((y * y).mean(axis=1, keepdims=True) + eps)
                 out["dgamma"][h] += (dz * y * r * c).sum(axis=0)
                 gd = c * g[h][None, :] * dz

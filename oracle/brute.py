@@ -59,6 +59,9 @@ def diff_attention(Q1: Matrix, K1: Matrix, Q2: Matrix, K2: Matrix, V: Matrix, la
     for i in range(len(W)):
         row = [math.fsum(W[i][j] * V[j][c] for j in range(len(V))) for c in range(d_v)]
         if norm:
+            if norm == "group":  # mean-subtracting variant, one group per head
+                mu = math.fsum(row) / d_v
+                row = [x - mu for x in row]
             rms = math.sqrt(math.fsum(x * x for x in row) / d_v + eps)
             row = [x / rms * gamma[c] * (1.0 - lambda_init) for c, x in enumerate(row)]
         out.append(row)

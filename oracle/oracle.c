@@ -19,6 +19,8 @@
  *   [VV] same lesson, "V1 vs V2": V1 applies a per-head RMSNorm after the
  *        difference; V2 drops it and keeps the KV heads of GQA while doubling
  *        the query heads.
+ *   [HF] the community post on the DIFF Transformer: GroupNorm for each head
+ *        (the mean-subtracting variant of the per-head norm).
  *   [AV] lesson "Attention Variants" (phase 7 lesson 15), "Build it", step 1:
  *        the causal mask admits key j for query i iff j <= i; step 2 and the
  *        sliding-window figure of its "Concept" section: a causal window of W
@@ -124,8 +126,16 @@ static void diff_row(const float *q1, const float *q2,
         for (int c = 0; c < d_v; ++c)
             y[c] += w * (double)vr[c];
     }
-    /* [VV] V1: per-head RMSNorm after the difference, scaled by (1 - lambda_init) */
+    /* [VV] V1: per-head norm after the difference, scaled by (1 - lambda_init):
+     * norm 1 RMSNorm; norm 2 GroupNorm with one group per head ([HF]): the
+     * channel mean is subtracted first and the variance replaces the mean square */
     if (norm) {
+        double mu = 0.0;
+        if (norm == 2) {
+            for (int c = 0; c < d_v; ++c) mu += y[c];
+            mu /= (double)d_v;
+            for (int c = 0; c < d_v; ++c) y[c] -= mu;
+        }
         double ms = 0.0;
         for (int c = 0; c < d_v; ++c) ms += y[c] * y[c];
         ms /= (double)d_v;
@@ -213,7 +223,7 @@ int oracle_decode(const float *q1, const float *q2, const float *k1c,
     if (B < 0 || H <= 0 || H_kv <= 0 || d_qk <= 0 || d_v <= 0 || page <= 0) return -1;
     if (window < 0) return -1;
     if (H % H_kv != 0) return -1;
-    if (norm && !gamma) return -1;
+    if (norm < 0 || norm > 2 || (norm && !gamma)) return -1;
     const int group = H / H_kv;
     const double init = oracle_lambda_init(depth);
     int64_t maxlen = (int64_t)max_pages * page;

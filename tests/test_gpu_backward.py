@@ -161,3 +161,19 @@ def test_backward_prefill_v1_shape_sampled_heads(torch, da):
                                   causal=True, norm=True, gamma=p.gamma[h:h + 1], eps=p.eps)
         for name in ("dq1", "dq2", "dk1", "dk2", "dv"):
             _grad_check(sl(g[name].cpu().numpy()), ref[name], f"{name} (b {b}, h {h})")
+
+
+@pytest.mark.parametrize("form", ["v1", "v2"])
+def test_backward_group_norm(torch, da, form):
+    p = _case(form, 200, True, seed=41)
+    if not p.norm:
+        p.gamma = np.random.default_rng(41).uniform(0.9, 1.1, (p.H, p.d_v)).astype(np.float32)
+    p.norm = "group"
+    say(f"backward {form} GroupNorm")
+    _, _, g, ref = _run(torch, da, p, seed=41)
+    for name in ("dq1", "dq2", "dv"):
+        _grad_check(g[name].cpu().numpy(), ref[name], name)
+    dg = g["dgamma"].cpu().numpy()
+    assert np.linalg.norm(dg - ref["dgamma"]) <= 1e-2 * np.linalg.norm(ref["dgamma"])
+    dl = g["dlambda"].cpu().numpy()
+    assert np.all(np.abs(dl - ref["dlambda"]) <= 1e-2 * np.abs(ref["dlambda"]).max() + 1e-6)

@@ -277,3 +277,11 @@ def test_decode_window_at_least_len_is_plain_bitwise(torch, da):
     plain = c.run().clone()
     for w in (1000, 1024, 1 << 20):
         assert torch.equal(c.run(window=w), plain), w
+
+
+def test_decode_v1_group_norm(torch, da):
+    d = small_v1([300, 64, 1, 700, 129], seed=70)
+    d.norm = "group"
+    c = DecodeCase(d, torch, da)
+    say("decode V1 GroupNorm")
+    check(c.run().float().cpu().numpy(), c.oracle(), "bf16", "decode V1 GroupNorm")

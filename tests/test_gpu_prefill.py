@@ -229,3 +229,21 @@ def test_bf16_long_sequence_small_window_sampled(torch, da):
     out = c.run(window=1024)
     rows = sampled_rows(p.B, p.H, p.N, seed=31, n_rand=24, edge=8)
     check(gather_rows(out, rows, p.H, p.N), c.oracle(rows=rows, window=1024), "bf16", "v2 W=1024")
+
+
+# ---------------------------------------------------------------- GroupNorm variant of the V1 norm
+
+@pytest.mark.parametrize("form,shared,N", [("v1", False, 200), ("v1", True, 333), ("v2", True, 150)])
+def test_bf16_group_norm(torch, da, form, shared, N):
+    p = _bf16_case(form, N, True, seed=N, shared=shared, norm=True)
+    p.norm = "group"
+    c = PrefillCase(p)
+    say(f"bf16 {form} shared_k {shared} N {N} GroupNorm")
+    check(c.run().float().cpu().numpy(), c.oracle(), "bf16", f"{form} GroupNorm")
+
+
+def test_fp32_group_norm(torch, da):
+    p = W.tiny_v1(seed=4, N=100, H=2)
+    p.norm = "group"
+    c = PrefillCase(p)
+    check(c.run().cpu().numpy(), c.oracle(), "f32", "f32 GroupNorm")

@@ -531,3 +531,56 @@ def test_swa_needs_causal():
     x = rnd(rng, 1, 1, 4, 2)
     with pytest.raises(ValueError):
         _prefill(x, x, x, x, x, [0.1], causal=False, norm=False, window=2)
+
+
+# --------------------------------------------------------------------------
+# GroupNorm variant of the V1 norm (one group per head, mean subtracted;
+# the community post on the DIFF Transformer)
+# --------------------------------------------------------------------------
+
+
+def test_group_norm_closed_form():
+    rng = np.random.default_rng(60)
+    B, H, N, d, dv = 1, 2, 9, 4, 8
+    q1, q2, k1, k2 = (rnd(rng, B, H, N, d) for _ in range(4))
+    v = rnd(rng, B, H, N, dv)
+    lam = [0.4, 0.9]
+    ones = np.ones((H, dv), np.float32)
+    plain = _prefill(q1, q2, k1, k2, v, lam, causal=True, norm=False, depth=5)
+    got = _prefill(q1, q2, k1, k2, v, lam, causal=True, norm="group", gamma=ones, depth=5, eps=1e-5)
+    u = plain - plain.mean(axis=-1, keepdims=True)
+    var = (u * u).mean(axis=-1, keepdims=True)
+    ref = u / np.sqrt(var + 1e-5) * (1 - oracle.lambda_init(5))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    assert np.all(np.abs(got.mean(axis=-1)) <= 1e-14)
+
+
+def test_group_norm_ignores_a_constant_added_to_v_rms_does_not():
+    # adding c to every value channel shifts y by (1 - lambda) c in every
+    # channel (each row of A1 - lambda A2 sums to 1 - lambda): the mean
+    # subtraction removes it exactly, the RMS norm does not
+    rng = np.random.default_rng(61)
+    B, H, N, d, dv = 1, 1, 12, 4, 6
+    q1, q2, k1, k2 = (rnd(rng, B, H, N, d) for _ in range(4))
+    v = np.round(rnd(rng, B, H, N, dv) * 64) / 64  # on a 1/64 grid, so v + 0.75 is exact in fp32
+    g = rng.uniform(0.9, 1.1, (H, dv)).astype(np.float32)
+    kw = dict(causal=True, gamma=g, depth=3)
+    a = _prefill(q1, q2, k1, k2, v, [0.3], norm="group", **kw)
+    b = _prefill(q1, q2, k1, k2, v + np.float32(0.75), [0.3], norm="group", **kw)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    ra = _prefill(q1, q2, k1, k2, v, [0.3], norm=True, **kw)
+    rb = _prefill(q1, q2, k1, k2, v + np.float32(0.75), [0.3], norm=True, **kw)
+    assert np.abs(ra - rb).max() > 1e-2
+
+
+def test_group_norm_matches_brute():
+    rng = np.random.default_rng(62)
+    N, d, dv = 7, 3, 5
+    q1, q2, k1, k2 = (rnd(rng, 1, 1, N, d) for _ in range(4))
+    v = rnd(rng, 1, 1, N, dv)
+    g = rng.uniform(0.5, 1.5, (1, dv)).astype(np.float32)
+    got = _prefill(q1, q2, k1, k2, v, [0.6], causal=True, norm="group", gamma=g, depth=4)
+    L = lambda x: x[0, 0].astype(np.float64).tolist()
+    ref = brute.diff_attention(L(q1), L(k1), L(q2), L(k2), L(v), 0.6, causal=True, norm="group",
+                               gamma=g[0].astype(np.float64).tolist(), lambda_init=brute.lambda_init(4))
+    np.testing.assert_allclose(got[0, 0], np.array(ref), rtol=1e-12, atol=1e-13)

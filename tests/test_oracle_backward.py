@@ -40,6 +40,7 @@ CASES = [
     dict(B=1, H=2, Hkv=1, N=6, dqk=4, dv=3, causal=True, norm=True, window=0),
     dict(B=2, H=2, Hkv=2, N=4, dqk=2, dv=3, causal=False, norm=True, window=0),
     dict(B=1, H=2, Hkv=2, N=7, dqk=3, dv=2, causal=True, norm=False, window=3),
+    dict(B=1, H=2, Hkv=1, N=6, dqk=3, dv=4, causal=True, norm="group", window=0),
 ]
 
 
