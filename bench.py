@@ -66,7 +66,7 @@ def decode_bytes(d):
     the page-table entries used and ctx_len (plus gamma for the V1 norm)."""
     L = d.ctx_len.astype(np.int64)
     nk = 1 if d.shared_k else 2
-    kv = int(L.sum()) * d.H_kv * (nk * d.d_qk + d.d_v) * 2
+    kv = int(L.sum()) * d.H_kv * (nk * d.d_qk + d.d_v) * d.kv_bytes  # bf16: 2 bytes, fp8: 1
     q = d.B * 2 * d.H * d.d_qk * 2
     out = d.B * d.H * d.d_v * 2
     table = int(((L + d.page - 1) // d.page).sum()) * 4 + d.B * 4
@@ -81,6 +81,7 @@ KERNEL_SOURCES = {
     "longctx_v1": ["prefill_bf16.hip", "tiles.hpp", "common.hpp"],
     "decode_v2": ["decode.hip", "common.hpp"],
     "decode_v1": ["decode.hip", "common.hpp"],
+    "decode_v2_fp8": ["decode.hip", "common.hpp"],
     "backward_v1": ["backward.hip", "tiles.hpp", "common.hpp"],
     "backward_v2": ["backward.hip", "tiles.hpp", "common.hpp"],
 }
@@ -152,26 +153,31 @@ def single_workload(args, torch, da, W, dev):
         call = lambda: dst.copy_(src)
         work, unit, metric, bound = 2.0 * n * 2, "GB/s", "device copy GB/s (read + write)", "hbm"
         desc = "torch copy_ of 2^31 bf16 elements (4 GiB read, 4 GiB written)"
-    elif name in ("decode_v2", "decode_v1"):
+    elif name in ("decode_v2", "decode_v1", "decode_v2_fp8"):
         d = getattr(W, name)()
         if d.q_full is not None:
             qd = to_dev(d.q_full)
             q1, q2 = qd[:, 0::2], qd[:, 1::2]
         else:
             q1, q2 = to_dev(d.q1), to_dev(d.q2)
-        kc, vc = to_dev(d.k1_cache), to_dev(d.v_cache)
-        kc2 = None if d.shared_k else to_dev(d.k2_cache)
+        kv = "bf16" if d.kv_dtype == "bf16" else "u8"  # fp8 caches as their uint8 codes
+        kc, vc = to_dev(d.k1_cache, kv), to_dev(d.v_cache, kv)
+        kc2 = None if d.shared_k else to_dev(d.k2_cache, kv)
         table, ctx = torch.from_numpy(d.page_table).to(dev), torch.from_numpy(d.ctx_len).to(dev)
         lam = da.lambda_(*(torch.from_numpy(x).to(dev) for x in (d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2)), d.depth)
         gamma = torch.from_numpy(d.gamma).to(dev) if d.norm else None
         out = torch.empty((d.B, d.H, d.d_v), dtype=torch.bfloat16, device=dev)
-        kw = dict(depth=d.depth, norm=d.norm, gamma=gamma, eps=d.eps, k2_cache=kc2)
+        kw = dict(depth=d.depth, norm=d.norm, gamma=gamma, eps=d.eps, k2_cache=kc2, k_scale=d.k_scale,
+                  v_scale=d.v_scale)
         ws = torch.empty(da.decode_workspace_bytes(q1, q2, kc, vc, table, ctx, lam, **kw),
                          dtype=torch.uint8, device=dev)
         call = lambda: da.decode(q1, q2, kc, vc, table, ctx, lam, out=out, workspace=ws, **kw)
         work, unit, metric, bound = decode_bytes(d), "GB/s", "decode GB/s (algorithmic HBM bytes)", "hbm"
         if name == "decode_v2":
             desc = "decode_v2: V2 paged decode, 64 seqs, ctx U{8192..32768}, 8 KV / 64 Q heads, d 128, page 64"
+        elif name == "decode_v2_fp8":
+            desc = ("decode_v2_fp8: decode_v2 with an fp8 e4m3 KV cache (per-tensor scales), bf16 queries "
+                    "and output")
         else:
             desc = ("decode_v1: V1 paged decode, 64 seqs, ctx U{8192..32768}, 8 KV / 32 heads, d_qk 64 "
                     "(K1, K2 caches), d_v 128, page 64, RMS norm")
@@ -259,13 +265,13 @@ def main():
                     help="profiling aid: run only one part of the step")
     ap.add_argument("--workload", default="step",
                     choices=["step", "prefill_v1", "prefill_v2", "longctx_v1", "tiny_v1", "decode_v2",
-                             "decode_v1", "backward_v1", "backward_v2", "copy"],
+                             "decode_v1", "decode_v2_fp8", "backward_v1", "backward_v2", "copy"],
                     help="step: the whole path (default); otherwise time one workload alone "
                          "(copy: a plain device copy of 4 GiB, for calibrating HBM byte counters)")
     ap.add_argument("--window", type=int, default=0,
                     help="causal sliding window for a single prefill workload (0 = none)")
     args = ap.parse_args()
-    if args.window and args.workload in ("step", "copy", "decode_v2", "decode_v1", "tiny_v1"):
+    if args.window and args.workload in ("step", "copy", "decode_v2", "decode_v1", "decode_v2_fp8", "tiny_v1"):
         ap.error("--window applies to a single prefill workload")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "

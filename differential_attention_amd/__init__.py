@@ -13,6 +13,11 @@ Functions (same names as the C entry points, without the prefix):
   prefill(q1, q2, k1, k2, v, lam, ...)           -> [B, H, N, d_v]
   decode_workspace_bytes(...)                    -> int
   decode(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, ...) -> [B, H, d_v]
+                                                 (bf16 or fp8 e4m3 KV caches)
+  prefill_stats(q1, v)                           -> fp32 buffers for the backward
+  backward_workspace_bytes(...)                  -> int
+  backward(q1, q2, k1, k2, v, lam, stats, dout, ...) -> dict of gradients
+  lambda_backward(lq1, lk1, lq2, lk2, dlambda)   -> dict of gradients
 """
 from __future__ import annotations
 
@@ -24,7 +29,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdiffattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
-BF16, F32 = 0, 1
+BF16, F32, FP8_E4M3 = 0, 1, 2
 NORM_NONE, NORM_RMS, NORM_GROUP = 0, 1, 2
 
 
@@ -120,6 +125,8 @@ class DecodeArgs(ctypes.Structure):
         ("split_pages", ctypes.c_int),
         ("dev_err", ctypes.c_void_p),
         ("window", ctypes.c_int),
+        ("kv_dtype", ctypes.c_int),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
     ]
 
 
@@ -184,6 +191,18 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.float32:
         return F32
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _kv_dtype_code(*caches) -> int:
+    """Storage of the KV caches: all bf16, or all fp8 e4m3 (torch.float8_e4m3fn,
+    or uint8 tensors holding the codes)."""
+    import torch
+    kinds = {c.dtype for c in caches if c is not None}
+    if kinds == {torch.bfloat16}:
+        return BF16
+    if kinds <= {torch.float8_e4m3fn, torch.uint8}:
+        return FP8_E4M3
+    raise TypeError(f"KV caches must all be bf16 or all fp8 e4m3, got {sorted(map(str, kinds))}")
 
 
 def _ptr(t) -> Optional[int]:
@@ -333,7 +352,8 @@ def lambda_backward(lq1, lk1, lq2, lk2, dlambda, stream=None):
 
 
 def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
-                 scale, out, split_pages, dev_err, k2_cache=None, window=0) -> DecodeArgs:
+                 scale, out, split_pages, dev_err, k2_cache=None, window=0, k_scale=1.0,
+                 v_scale=1.0) -> DecodeArgs:
     B, H, dqk = q1.shape
     P, Hkv, page, _ = k_cache.shape
     dv = v_cache.shape[3]
@@ -367,34 +387,40 @@ def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm
     a.split_pages = int(split_pages)
     a.dev_err = _ptr(dev_err)
     a.window = int(window)
+    a.kv_dtype = _kv_dtype_code(k_cache, k2_cache, v_cache)
+    a.k_scale, a.v_scale = float(k_scale), float(v_scale)
     return a
 
 
 def decode_workspace_bytes(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int,
                            norm: bool = False, gamma=None, eps: float = 1e-5, scale: float = 0.0,
-                           split_pages: int = 0, k2_cache=None, window: int = 0) -> int:
+                           split_pages: int = 0, k2_cache=None, window: int = 0, k_scale: float = 1.0,
+                           v_scale: float = 1.0) -> int:
     a = _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
-                     scale, None, split_pages, None, k2_cache, window)
+                     scale, None, split_pages, None, k2_cache, window, k_scale, v_scale)
     return int(load_library().diffattn_decode_workspace_bytes(ctypes.byref(a)))
 
 
 def decode(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int, norm: bool = False,
            gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, workspace=None,
-           split_pages: int = 0, dev_err=None, stream=None, k2_cache=None, window: int = 0):
+           split_pages: int = 0, dev_err=None, stream=None, k2_cache=None, window: int = 0,
+           k_scale: float = 1.0, v_scale: float = 1.0):
     """Paged decode (one query token per sequence).
 
     q1, q2 [B, H, d_qk]; k_cache [num_pages, H_kv, page, d_qk] and v_cache
     [num_pages, H_kv, page, d_v] contiguous; k_cache serves both branches
     unless k2_cache (the branch-2 keys, V1 form with d_qk 64) is given;
     page_table [B, max_pages] int32; ctx_len [B] int32; lam [H] fp32;
-    window > 0: the query sees its last window tokens. Returns out [B, H, d_v]."""
+    window > 0: the query sees its last window tokens. The caches are bf16, or
+    fp8 e4m3 (float8_e4m3fn or uint8 codes) read as k_scale * code and
+    v_scale * code. Returns out [B, H, d_v]."""
     import torch
     B, H, _ = q1.shape
     dv = v_cache.shape[3]
     if out is None:
         out = torch.empty((B, H, dv), dtype=q1.dtype, device=q1.device)
     a = _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
-                     scale, out, split_pages, dev_err, k2_cache, window)
+                     scale, out, split_pages, dev_err, k2_cache, window, k_scale, v_scale)
     lib = load_library()
     need = int(lib.diffattn_decode_workspace_bytes(ctypes.byref(a)))
     if workspace is None:

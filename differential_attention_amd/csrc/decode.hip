@@ -48,6 +48,15 @@
 // *dev_err is set. With a causal window W the query sees tokens L-W .. L-1
 // (lesson "Attention Variants", sliding window, for the last row): only the
 // pages holding them enter the page list and earlier tokens are masked.
+//
+// fp8 caches (OCP e4m3, per-tensor scales): every lane loads 16 codes per
+// 16-byte request -- half the bytes of a bf16 slice, so twice the pages are
+// held in flight in the same registers -- and widens them to bf16 on the way
+// to the matrix cores (exact: every e4m3 value is a bf16 value). The key
+// scale is folded into the score scale and the value scale applied in the
+// combine, so the loop itself runs on the codes' values. Because a dot
+// product does not care in which order its features are summed, a lane loads
+// 32 contiguous key features and the Q fragments use the same feature order.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -86,6 +95,7 @@ struct DecodeParams {
     int *dev_err;
     int B, H, H_kv, group, qrows, max_pages, num_pages, target, num_wgs, norm, window;
     float sc_log2, eps, one_minus_init;
+    float v_scale;  // fp8 value scale (1 for bf16 caches)
 };
 
 __device__ __forceinline__ uint4 ldg16(const __bf16 *p) { return *(const uint4 *)p; }
@@ -139,14 +149,36 @@ __device__ __forceinline__ int block_scan(int x, int *sh, int *total) {
 }
 
 // one wave's 16-token slice of a page: K operands and V rows
+template <bool FP8>
 struct Slice {
     uint4 k[4];  // k[kc]: token 16 w + lane % 16, 8 features from 8 (lane / 16) (see the Q fragments)
     uint4 v[4];  // v[i]: token 16 w + 4 i + lane / 16, features 8 (lane % 16) .. +7
     bool ok;     // the page id was valid
 };
+template <>
+struct Slice<true> {
+    uint4 k[2];  // token 16 w + lane % 16; d_qk 128: features 32 (lane / 16) .. +31;
+                 // d_qk 64: k[0] from K1, k[1] from K2, features 16 (lane / 16) .. +15
+    uint4 v[2];  // v[i]: token 16 w + 8 i + lane / 8, features 16 (lane % 8) .. +15
+    bool ok;
+};
 
-template <int DQK>
+// 4 e4m3 codes (in memory order) -> 4 bf16 values in the same order
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);  // bytes 0, 1
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);   // bytes 2, 3
+    return uint2{__builtin_bit_cast(uint32_t, pack2(a[0], a[1])), __builtin_bit_cast(uint32_t, pack2(b[0], b[1]))};
+}
+
+// 8 codes (two words) -> one bf16x8 MFMA operand
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const uint2 a = e4m3x4_to_bf16(w0), b = e4m3x4_to_bf16(w1);
+    return as_bf16x8(uint4{a.x, a.y, b.x, b.y});
+}
+
+template <int DQK, bool FP8>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
+    constexpr int kBufT = FP8 ? 2 * kBuf : kBuf;  // slices in flight per wave
     __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * 16 * kDV * 4];  // 32 KB
     __shared__ float red_m[4][16], red_l[4][16];
     __shared__ int sh[4], s_b, s_excl;
@@ -207,9 +239,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 
         // Q^T fragments: lane supplies query row n (pair n / 2, branch n % 2).
         // d_qk 128: k step kc covers features 32 kc + 8 grp .. +7 of the shared
-        // keys. d_qk 64: k steps 0, 1 contract K1 with the branch-1 rows and
-        // steps 2, 3 contract K2 with the branch-2 rows (each with the other
-        // branch's rows zero), so one accumulator gets each row's own scores.
+        // keys (fp8: 32 grp + 8 kc .. +7). d_qk 64: k steps 0, 1 contract K1
+        // with the branch-1 rows and steps 2, 3 contract K2 with the branch-2
+        // rows (each with the other branch's rows zero), so one accumulator
+        // gets each row's own scores; features 32 (kc % 2) + 8 grp .. +7
+        // (fp8: 16 grp + 8 (kc % 2) .. +7).
         bf16x8 qf[4];
         {
             const bool ok = n < p.qrows;
@@ -220,7 +254,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
             for (int kc = 0; kc < 4; ++kc) {
                 uint4 z = {0u, 0u, 0u, 0u};
                 const bool use = DQK == 128 ? ok : (ok && br == (kc >> 1));
-                qf[kc] = as_bf16x8(use ? ldg16(q + 32 * (DQK == 128 ? kc : (kc & 1)) + 8 * grp) : z);
+                int f;
+                if (FP8)
+                    f = DQK == 128 ? 32 * grp + 8 * kc : 16 * grp + 8 * (kc & 1);
+                else
+                    f = 32 * (DQK == 128 ? kc : (kc & 1)) + 8 * grp;
+                qf[kc] = as_bf16x8(use ? ldg16(q + f) : z);
             }
         }
 
@@ -237,49 +276,88 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         for (int c0 = p0; c0 < p1; c0 += 64) {
             const int np = min(64, p1 - c0);
             const int ids = lane < np ? table[c0 + lane] : 0;
-            auto load = [&](Slice &S, int k) {
+            auto load = [&](Slice<FP8> &S, int k) {
                 int phys = __builtin_amdgcn_readlane(ids, k);
                 S.ok = phys >= 0 && phys < p.num_pages;
                 bad_page |= !S.ok;
                 phys = S.ok ? phys : 0;
                 const int64_t row0 = ((int64_t)phys * p.H_kv + g) * kPage + 16 * wave;  // first token row
-                const __bf16 *vp = p.vc + row0 * kDV + grp * kDV + 8 * n;
-                if (DQK == 128) {
-                    const __bf16 *kp = p.kc + (row0 + n) * DQK + 8 * grp;
-#pragma unroll
-                    for (int kc = 0; kc < 4; ++kc) S.k[kc] = ldg16(kp + 32 * kc);
+                if constexpr (FP8) {
+                    const unsigned char *vp = (const unsigned char *)p.vc + (row0 + (lane >> 3)) * kDV + 16 * (lane & 7);
+                    if (DQK == 128) {
+                        const unsigned char *kp = (const unsigned char *)p.kc + (row0 + n) * DQK + 32 * grp;
+                        S.k[0] = *(const uint4 *)kp;
+                        S.k[1] = *(const uint4 *)(kp + 16);
+                    } else {
+                        const int64_t off = (row0 + n) * DQK + 16 * grp;
+                        S.k[0] = *(const uint4 *)((const unsigned char *)p.kc + off);
+                        S.k[1] = *(const uint4 *)((const unsigned char *)p.kc2 + off);
+                    }
+                    S.v[0] = *(const uint4 *)vp;
+                    S.v[1] = *(const uint4 *)(vp + 8 * kDV);
                 } else {
-                    const __bf16 *kp1 = p.kc + (row0 + n) * DQK + 8 * grp;
-                    const __bf16 *kp2 = p.kc2 + (row0 + n) * DQK + 8 * grp;
-                    S.k[0] = ldg16(kp1);
-                    S.k[1] = ldg16(kp1 + 32);
-                    S.k[2] = ldg16(kp2);
-                    S.k[3] = ldg16(kp2 + 32);
-                }
+                    const __bf16 *vp = p.vc + row0 * kDV + grp * kDV + 8 * n;
+                    if (DQK == 128) {
+                        const __bf16 *kp = p.kc + (row0 + n) * DQK + 8 * grp;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S.v[i] = ldg16(vp + 4 * i * kDV);
+                        for (int kc = 0; kc < 4; ++kc) S.k[kc] = ldg16(kp + 32 * kc);
+                    } else {
+                        const __bf16 *kp1 = p.kc + (row0 + n) * DQK + 8 * grp;
+                        const __bf16 *kp2 = p.kc2 + (row0 + n) * DQK + 8 * grp;
+                        S.k[0] = ldg16(kp1);
+                        S.k[1] = ldg16(kp1 + 32);
+                        S.k[2] = ldg16(kp2);
+                        S.k[3] = ldg16(kp2 + 32);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S.v[i] = ldg16(vp + 4 * i * kDV);
+                }
             };
 
-            auto process = [&](const Slice &S, int k) {
+            auto process = [&](const Slice<FP8> &S, int k) {
                 const int pg = fp + c0 + k;                   // page index in the sequence
                 const int vis = L - pg * kPage - 16 * wave;   // rows >= vis are past the end
                 const int vlo = t0 - pg * kPage - 16 * wave;  // rows < vlo are before the window
                 // V rows into the wave buffer (rows past the end as zeros)
+                if constexpr (FP8) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 4 * i + grp;
-                    const uint32_t keep = (row < vis && row >= vlo) ? 0xffffffffu : 0u;  // select by value
-                    uint4 v = S.v[i];
-                    v.x &= keep;
-                    v.y &= keep;
-                    v.z &= keep;
-                    v.w &= keep;
-                    *(uint4 *)(vbuf + row * 256 + 16 * (n ^ ((row & 7) << 1))) = v;
+                    for (int i = 0; i < 2; ++i) {
+                        const int row = 8 * i + (lane >> 3);
+                        const uint32_t keep = (row < vis && row >= vlo) ? 0xffffffffu : 0u;
+                        const uint2 a = e4m3x4_to_bf16(S.v[i].x), b2 = e4m3x4_to_bf16(S.v[i].y);
+                        const uint2 c2 = e4m3x4_to_bf16(S.v[i].z), d2 = e4m3x4_to_bf16(S.v[i].w);
+                        // features 16 (lane % 8) .. +15 are 16-byte chunks 2 (lane % 8) and
+                        // 2 (lane % 8) + 1 of the row; the swizzle is even, so they stay adjacent
+                        unsigned char *dst = vbuf + row * 256 + 16 * ((2 * (lane & 7)) ^ ((row & 7) << 1));
+                        *(uint4 *)dst = uint4{a.x & keep, a.y & keep, b2.x & keep, b2.y & keep};
+                        *(uint4 *)(dst + 16) = uint4{c2.x & keep, c2.y & keep, d2.x & keep, d2.y & keep};
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 4 * i + grp;
+                        const uint32_t keep = (row < vis && row >= vlo) ? 0xffffffffu : 0u;  // select by value
+                        uint4 v = S.v[i];
+                        v.x &= keep;
+                        v.y &= keep;
+                        v.z &= keep;
+                        v.w &= keep;
+                        *(uint4 *)(vbuf + row * 256 + 16 * (n ^ ((row & 7) << 1))) = v;
+                    }
                 }
                 // scores of the 16 tokens against the 16 query rows
                 f32x4 sc = f32x4{};
 #pragma unroll
-                for (int kc = 0; kc < 4; ++kc) sc = mfma16(as_bf16x8(S.k[kc]), qf[kc], sc);
+                for (int kc = 0; kc < 4; ++kc) {
+                    bf16x8 ka;
+                    if constexpr (FP8) {
+                        const uint4 &w = S.k[kc >> 1];
+                        ka = (kc & 1) ? e4m3x8_to_bf16(w.z, w.w) : e4m3x8_to_bf16(w.x, w.y);
+                    } else {
+                        ka = as_bf16x8(S.k[kc]);
+                    }
+                    sc = mfma16(ka, qf[kc], sc);
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (!S.ok || 4 * grp + r >= vis || 4 * grp + r < vlo) sc[r] = -INFINITY;
@@ -314,17 +392,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 __builtin_amdgcn_s_waitcnt(0xC07F);
             };
 
-            Slice S[kBuf];
+            Slice<FP8> S[kBufT];
 #pragma unroll
-            for (int j = 0; j < kBuf; ++j)
+            for (int j = 0; j < kBufT; ++j)
                 if (j < np) load(S[j], j);
-            for (int k0 = 0; k0 < np; k0 += kBuf) {
+            for (int k0 = 0; k0 < np; k0 += kBufT) {
 #pragma unroll
-                for (int j = 0; j < kBuf; ++j) {
+                for (int j = 0; j < kBufT; ++j) {
                     const int k = k0 + j;
                     if (k < np) {
                         process(S[j], k);
-                        if (k + kBuf < np) load(S[j], k + kBuf);
+                        if (k + kBufT < np) load(S[j], k + kBufT);
                     }
                 }
             }
@@ -420,7 +498,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
             acc += rq[dv] * f;
             lsum += rq[kDV + 1] * f;
         }
-        ob[br] = lsum > 0.0f ? acc / lsum : 0.0f;
+        ob[br] = lsum > 0.0f ? acc / lsum * p.v_scale : 0.0f;
     }
     float y;
     {
@@ -445,7 +523,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
 
 // Work-groups of the split pass that fit on the device at once; cached per
 // device (compute-unit count times the kernel's occupancy per unit).
-template <int DQK>
+template <int DQK, bool FP8>
 int resident_split_wgs() {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cache[kMaxDevices];
@@ -457,7 +535,7 @@ int resident_split_wgs() {
     }
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<DQK>, 256, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<DQK, FP8>, 256, 0) != hipSuccess)
         return 1;
     const int r = std::max(1, cus * per_cu);
     if (dev >= 0 && dev < kMaxDevices) cache[dev].store(r, std::memory_order_relaxed);
@@ -495,19 +573,22 @@ hipError_t launch_decode_bf16(const diffattn_decode_args &a, const DecodePlan &p
     p.max_pages = a.max_pages;
     p.num_pages = a.num_pages;
     p.target = plan.target_pages;
-    const bool d64 = a.d_qk == 64;
-    p.num_wgs = plan.target_pages > 0
-                    ? plan.max_wgs
-                    : std::min(plan.max_wgs, kRounds * (d64 ? resident_split_wgs<64>() : resident_split_wgs<128>()));
+    const bool d64 = a.d_qk == 64, fp8 = a.kv_dtype == DIFFATTN_FP8_E4M3;
+    int resident;
+    if (fp8)
+        resident = d64 ? resident_split_wgs<64, true>() : resident_split_wgs<128, true>();
+    else
+        resident = d64 ? resident_split_wgs<64, false>() : resident_split_wgs<128, false>();
+    p.num_wgs = plan.target_pages > 0 ? plan.max_wgs : std::min(plan.max_wgs, kRounds * resident);
     p.norm = a.norm;  // 0 none, 1 RMS, 2 GroupNorm
     p.window = a.window;
-    p.sc_log2 = scale * kLog2e;
+    p.sc_log2 = scale * (fp8 ? a.k_scale : 1.0f) * kLog2e;
+    p.v_scale = fp8 ? a.v_scale : 1.0f;
     p.eps = a.eps;
     p.one_minus_init = 1.0f - lambda_init;
-    if (d64)
-        hipLaunchKernelGGL(decode_split_kernel<64>, dim3(p.num_wgs), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(decode_split_kernel<128>, dim3(p.num_wgs), dim3(256), 0, stream, p);
+    auto kern = fp8 ? (d64 ? decode_split_kernel<64, true> : decode_split_kernel<128, true>)
+                    : (d64 ? decode_split_kernel<64, false> : decode_split_kernel<128, false>);
+    hipLaunchKernelGGL(kern, dim3(p.num_wgs), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(a.H, a.B), dim3(128), 0, stream, p);

@@ -208,6 +208,11 @@ int check_decode_sizes(const diffattn_decode_args *a, DecodePlan *plan, std::str
     if (a->norm != DIFFATTN_NORM_NONE && !(a->eps > 0.0f && !isinf(a->eps)))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: eps must be finite and > 0");
     if (a->window < 0) return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: window must be >= 0");
+    if (a->kv_dtype != DIFFATTN_BF16 && a->kv_dtype != DIFFATTN_FP8_E4M3)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: kv_dtype must be bf16 or fp8 e4m3");
+    if (a->kv_dtype == DIFFATTN_FP8_E4M3 && !(a->k_scale > 0.0f && !isinf(a->k_scale) && a->v_scale > 0.0f &&
+                                               !isinf(a->v_scale)))
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: fp8 caches need finite k_scale, v_scale > 0");
     if (a->split_pages < 0 || a->split_pages > kDecodeMaxTarget)
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: split_pages must be in [0, 2^24]");
     if ((int64_t)a->B * a->max_pages > INT32_MAX)
@@ -264,12 +269,13 @@ int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *m
     if (!extent_of(a->out, 2, od, &eo) || !non_overlapping(od))
         return fail(msg, DIFFATTN_EINVAL, "diffattn_decode: bad output strides");
     const int64_t kv_elems = (int64_t)a->num_pages * a->H_kv * a->page_size;
+    const size_t kv_b = a->kv_dtype == DIFFATTN_FP8_E4M3 ? 1 : 2;
     struct R {
         const void *p;
         size_t bytes;
-    } rs[] = {{a->k1_cache, (size_t)kv_elems * a->d_qk * 2},
-              {a->k2_cache, (size_t)kv_elems * a->d_qk * 2},
-              {a->v_cache, (size_t)kv_elems * a->d_v * 2},
+    } rs[] = {{a->k1_cache, (size_t)kv_elems * a->d_qk * kv_b},
+              {a->k2_cache, (size_t)kv_elems * a->d_qk * kv_b},
+              {a->v_cache, (size_t)kv_elems * a->d_v * kv_b},
               {a->page_table, (size_t)a->B * a->max_pages * 4},
               {a->ctx_len, (size_t)a->B * 4},
               {a->lambda, (size_t)a->H * 4}};

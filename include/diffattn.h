@@ -52,7 +52,12 @@ enum {
     DIFFATTN_EHIP = -4          /* the HIP runtime reported an error */
 };
 
-enum { DIFFATTN_BF16 = 0, DIFFATTN_F32 = 1 };
+enum {
+    DIFFATTN_BF16 = 0,
+    DIFFATTN_F32 = 1,
+    DIFFATTN_FP8_E4M3 = 2  /* KV-cache storage only: OCP fp8 e4m3 (bias 7, no infinities,
+                              0x7f / 0xff are NaN), one byte per element */
+};
 enum {
     DIFFATTN_NORM_NONE = 0,  /* V2 */
     DIFFATTN_NORM_RMS = 1,   /* V1: y / sqrt(mean(y^2) + eps) * gamma * (1 - lambda_init) */
@@ -114,7 +119,7 @@ typedef struct {
  *   out         [B, H, d_v]                   strides so[0], so[1]
  * Supported: dtype DIFFATTN_BF16, d_v 128, page_size 64, H / H_kv <= 8
  * output heads per KV head, and d_qk 128 with k1_cache == k2_cache (V2) or
- * d_qk 64 with any two key caches (V1).
+ * d_qk 64 with any two key caches (V1); the caches bf16 or fp8 (kv_dtype).
  * split_pages: pages per work-group of the split-KV pass, 0..2^24. The pages
  * of all (sequence, KV head) pairs are cut into equal contiguous ranges, one
  * per work-group (at most 2048); 0 lets the library use one round of the
@@ -145,6 +150,12 @@ typedef struct {
     int split_pages;
     int *dev_err;
     int window;          /* 0: none; W > 0: the query sees tokens ctx_len-W .. ctx_len-1 */
+    /* KV-cache storage: DIFFATTN_BF16 (0), or DIFFATTN_FP8_E4M3 with one byte
+     * per element in the same layouts, the key caches dequantised as
+     * k_scale * code and the value cache as v_scale * code (per-tensor scales,
+     * finite and > 0; ignored for bf16). Queries and output stay bf16. */
+    int kv_dtype;
+    float k_scale, v_scale;
 } diffattn_decode_args;
 
 /*

@@ -198,10 +198,35 @@ def test_decode_workspace_and_plan(lib):
     ("split_pages", (1 << 24) + 1, da.EINVAL),
     ("window", -3, da.EINVAL),
     ("out", FAKE, da.EINVAL),           # overlaps q1
+    ("kv_dtype", da.F32, da.EINVAL),    # caches: bf16 or fp8 e4m3 only
+    ("kv_dtype", 3, da.EINVAL),
 ])
 def test_decode_rejects(lib, field, value, code):
     a = _decode_args(**{field: value})
     assert lib.diffattn_decode(ctypes.byref(a), FAKE + 6 * (1 << 34), 1 << 40, None) == code
+
+
+def test_decode_fp8_scales_and_extents(lib):
+    ws = FAKE + 6 * (1 << 34)
+    good = dict(kv_dtype=da.FP8_E4M3, k_scale=0.5, v_scale=0.25)
+    a = _decode_args(**good)
+    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == \
+        lib.diffattn_decode_workspace_bytes(ctypes.byref(_decode_args()))  # same records as bf16
+    for bad in (dict(k_scale=0.0), dict(v_scale=-1.0), dict(k_scale=float("inf")), dict(v_scale=float("nan"))):
+        a = _decode_args(**{**good, **bad})
+        assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) == 0, bad
+        assert lib.diffattn_decode(ctypes.byref(a), ws, 1 << 40, None) == da.EINVAL, bad
+        assert "scale" in lib.diffattn_last_error().decode()
+    # bf16 caches ignore the scales
+    a = _decode_args(k_scale=0.0, v_scale=0.0)
+    assert lib.diffattn_decode_workspace_bytes(ctypes.byref(a)) > 0
+    # the overlap check sizes the caches by their storage: one byte per fp8
+    # element, two per bf16 element
+    v_end8 = 20000 * 8 * 64 * 128
+    for kw in (dict(good, out=FAKE + 2 * (1 << 34) + v_end8 - 256), dict(out=FAKE + 2 * (1 << 34) + v_end8)):
+        a = _decode_args(**kw)
+        assert lib.diffattn_decode(ctypes.byref(a), ws, 1 << 40, None) == da.EINVAL
+        assert "overlaps" in lib.diffattn_last_error().decode()
 
 
 def test_decode_rejects_small_workspace(lib):

@@ -31,9 +31,10 @@ class DecodeCase:
             self.q1, self.q2 = qf[:, 0::2], qf[:, 1::2]
         else:
             self.q1, self.q2 = to_dev(d.q1, "bf16"), to_dev(d.q2, "bf16")
-        self.kc = to_dev(d.k1_cache, "bf16")
-        self.kc2 = None if d.shared_k else to_dev(d.k2_cache, "bf16")
-        self.vc = to_dev(d.v_cache, "bf16")
+        kv = "bf16" if d.kv_dtype == "bf16" else "u8"  # fp8 caches go in as their uint8 codes
+        self.kc = to_dev(d.k1_cache, kv)
+        self.kc2 = None if d.shared_k else to_dev(d.k2_cache, kv)
+        self.vc = to_dev(d.v_cache, kv)
         self.table = torch.from_numpy(d.page_table).to(dev())
         self.ctx = torch.from_numpy(d.ctx_len).to(dev())
         self.lam64 = oracle.lambda_(d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2, d.depth)
@@ -43,7 +44,8 @@ class DecodeCase:
 
     def run(self, **kw):
         d = self.d
-        args = dict(depth=d.depth, norm=d.norm, gamma=self.gamma, eps=d.eps, k2_cache=self.kc2)
+        args = dict(depth=d.depth, norm=d.norm, gamma=self.gamma, eps=d.eps, k2_cache=self.kc2,
+                    k_scale=d.k_scale, v_scale=d.v_scale)
         args.update(kw)
         return self.da.decode(self.q1, self.q2, self.kc, self.vc, self.table, self.ctx, self.lam, **args)
 
@@ -65,9 +67,9 @@ class DecodeCase:
         table = np.full((len(seqs), d.max_pages), -1, np.int32)
         for r, (b, n) in enumerate(zip(seqs, npg)):
             table[r, :n] = [remap[int(p)] for p in d.page_table[b, :n]]
-        kc = W.bf16_to_f32(d.k1_cache[used])
-        kc2 = W.bf16_to_f32(d.k2_cache[used])
-        vc = W.bf16_to_f32(d.v_cache[used])
+        kc = d.values("k1_cache", d.k1_cache[used])
+        kc2 = d.values("k2_cache", d.k2_cache[used])
+        vc = d.values("v_cache", d.v_cache[used])
         return oracle.decode(d.f32("q1")[seqs], d.f32("q2")[seqs], kc, kc2, vc, table, d.ctx_len[seqs],
                              self.lam64, depth=d.depth, norm=norm, gamma=gamma, window=window)
 
@@ -285,3 +287,97 @@ def test_decode_v1_group_norm(torch, da):
     c = DecodeCase(d, torch, da)
     say("decode V1 GroupNorm")
     check(c.run().float().cpu().numpy(), c.oracle(), "bf16", "decode V1 GroupNorm")
+
+
+# ---- fp8 (OCP e4m3) KV caches with per-tensor scales; the oracle reads the
+# dequantised values (scale * code), exactly what the kernel contracts with
+
+
+def small_fp8(lens, H=8, H_kv=2, seed=0, max_pages=16, form="v2"):
+    mk = W.decode_v1 if form == "v1" else W.decode_v2
+    return mk(seed=seed, B=len(lens), H=H, H_kv=H_kv, max_pages=max_pages, ctx_len=np.array(lens),
+              kv_dtype="fp8")
+
+
+@pytest.mark.parametrize("form", ["v2", "v1"])
+@pytest.mark.parametrize("lens", [[1, 63, 64, 65, 128, 1000], [1024, 777, 5, 129]])
+@pytest.mark.parametrize("split_pages", [0, 1, 3, 1 << 20])
+def test_decode_fp8_ragged(torch, da, form, lens, split_pages):
+    c = DecodeCase(small_fp8(lens, seed=80, form=form), torch, da)
+    say(f"decode fp8 {form} lens {lens} split_pages {split_pages}")
+    check(c.run(split_pages=split_pages).float().cpu().numpy(), c.oracle(), "bf16", f"decode fp8 {form}")
+
+
+@pytest.mark.parametrize("form,H,H_kv", [("v2", 8, 8), ("v2", 16, 2), ("v2", 6, 2), ("v1", 16, 2), ("v1", 4, 4)])
+def test_decode_fp8_groupings(torch, da, form, H, H_kv):
+    c = DecodeCase(small_fp8([300, 64, 1, 700, 129], H=H, H_kv=H_kv, seed=81 + H, form=form), torch, da)
+    say(f"decode fp8 {form} H {H} H_kv {H_kv}")
+    check(c.run().float().cpu().numpy(), c.oracle(), "bf16", "decode fp8 grouping")
+
+
+@pytest.mark.parametrize("form", ["v2", "v1"])
+@pytest.mark.parametrize("window", [1, 65, 1000])
+def test_decode_fp8_sliding_window(torch, da, form, window):
+    c = DecodeCase(small_fp8([1, 63, 64, 65, 128, 1000, 333], seed=90 + window, form=form), torch, da)
+    say(f"decode fp8 {form} window {window}")
+    check(c.run(window=window).float().cpu().numpy(), c.oracle(window=window), "bf16",
+          f"decode fp8 {form} W={window}")
+
+
+def test_decode_fp8_group_norm(torch, da):
+    d = small_fp8([300, 64, 1, 700, 129], seed=95, form="v1")
+    d.norm = "group"
+    c = DecodeCase(d, torch, da)
+    check(c.run().float().cpu().numpy(), c.oracle(), "bf16", "decode fp8 V1 GroupNorm")
+
+
+def test_decode_fp8_scales_and_nan_codes_past_the_end(torch, da):
+    # other scales (k and v differ), and NaN codes (0x7f, 0xff) in the slots
+    # past every sequence's end: those tokens are masked, so they cannot reach
+    # the output
+    d = small_fp8([100, 64, 1, 250], seed=96)
+    d.k_scale, d.v_scale = 0.03125, 0.0125
+    for b, L in enumerate(d.ctx_len):
+        last = d.page_table[b, (L - 1) // 64]
+        tail = L % 64
+        if tail:
+            d.k1_cache[last, :, tail:] = 0x7f
+            d.v_cache[last, :, tail:] = 0xff
+    c = DecodeCase(d, torch, da)
+    got = c.run().float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    check(got, c.oracle(), "bf16", "decode fp8 scales / NaN tail")
+
+
+def test_decode_fp8_page_permutation_is_bitwise_invariant(torch, da):
+    d = small_fp8([200, 1000, 64, 5], seed=97)
+    c = DecodeCase(d, torch, da)
+    a = c.run().clone()
+    perm = np.random.default_rng(2).permutation(d.num_pages)
+    inv = np.argsort(perm)
+    kc = np.empty_like(d.k1_cache)
+    vc = np.empty_like(d.v_cache)
+    kc[inv] = d.k1_cache
+    vc[inv] = d.v_cache
+    table = np.where(d.page_table >= 0, inv[np.maximum(d.page_table, 0)], -1).astype(np.int32)
+    c.kc, c.vc = to_dev(kc, "u8"), to_dev(vc, "u8")
+    c.table = torch.from_numpy(table).to(dev())
+    assert torch.equal(a, c.run())
+
+
+def test_decode_fp8_float8_tensor_input(torch, da):
+    # torch.float8_e4m3fn caches are accepted as well as their uint8 codes
+    d = small_fp8([300, 64, 129], seed=98)
+    c = DecodeCase(d, torch, da)
+    a = c.run().clone()
+    c.kc, c.vc = c.kc.view(torch.float8_e4m3fn), c.vc.view(torch.float8_e4m3fn)
+    assert torch.equal(a, c.run())
+
+
+def test_decode_v2_fp8_full(torch, da):
+    d = W.decode_v2_fp8()
+    say(f"decode_v2_fp8 full: 64 sequences, {d.num_pages} pages")
+    c = DecodeCase(d, torch, da)
+    out = c.run().float().cpu().numpy()
+    seqs = np.array([0, 7, int(np.argmax(d.ctx_len)), int(np.argmin(d.ctx_len)), 33, 63])
+    check(out[seqs], c.oracle(seqs=seqs), "bf16", "decode_v2_fp8 sampled sequences")

@@ -21,6 +21,8 @@ d_head 128 shape, and its exercise on GQA with 8 KV heads and 32 query heads):
                    causal, bf16, d 128, depth 20.
 * ``decode_v2``    V2 paged decode, 64 sequences, context U{8192..32768},
                    page 64, 8 KV heads, 64 query heads, bf16, d 128, depth 20.
+* ``decode_v2_fp8`` the V2 decode with an fp8 (e4m3) KV cache, per-tensor
+                   scale 1/56 for K and for V.
 * ``decode_v1``    V1 paged decode, the same sequences and pages as the V2
                    decode's shape family with d_qk 64 (separate K1, K2 caches),
                    d_v 128, 32 heads over 8 KV heads, RMS norm, depth 12.
@@ -157,10 +159,64 @@ class Decode:
     eps: float = 1e-5
     shared_k: bool = True
     q_full: Optional[np.ndarray] = None  # [B, 2H, d]
+    kv_dtype: str = "bf16"               # or "fp8": the caches hold e4m3 codes (uint8)
+    k_scale: float = 1.0                 # fp8: key = k_scale * value of the code
+    v_scale: float = 1.0                 # fp8: value = v_scale * value of the code
+
+    @property
+    def kv_bytes(self) -> int:
+        return 1 if self.kv_dtype == "fp8" else 2
 
     def f32(self, name: str) -> np.ndarray:
-        a = getattr(self, name)
+        return self.values(name, getattr(self, name))
+
+    def values(self, name: str, a: np.ndarray) -> np.ndarray:
+        """fp32 values of array ``a`` stored as field ``name`` (a slice of a
+        cache, say): fp8 caches dequantised with their scale."""
+        if name.endswith("_cache") and self.kv_dtype == "fp8":
+            scale = self.v_scale if name == "v_cache" else self.k_scale
+            return fp8_to_f32(a) * np.float32(scale)
         return bf16_to_f32(a) if self.dtype == "bf16" else a
+
+
+# --------------------------------------------------------------------------
+# fp8, OCP e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits; no
+# infinities; S.1111.111 is NaN; the largest finite magnitude is 448
+# --------------------------------------------------------------------------
+
+FP8_MAX = 448.0
+
+
+def f32_to_fp8(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values inside [-448, 448] to e4m3 (nearest, ties to even);
+    returns the uint8 codes."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert np.all(np.abs(x) <= FP8_MAX)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _fp8_table() -> np.ndarray:
+    """The value of every e4m3 code, from the format's definition."""
+    t = np.empty(256, np.float32)
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            v = float("nan")
+        elif e == 0:
+            v = m / 8.0 * 2.0 ** -6
+        else:
+            v = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        t[c] = -v if s else v
+    return t
+
+
+FP8_TABLE = _fp8_table()
+
+
+def fp8_to_f32(codes: np.ndarray) -> np.ndarray:
+    """Exact values of e4m3 codes."""
+    return FP8_TABLE[np.asarray(codes, np.uint8)]
 
 
 def _lambda_vectors(rng, H, d_l):
@@ -222,9 +278,16 @@ def prefill_v2(seed: int = 3, B: int = 1, H: int = 32, H_kv: int = 8, N: int = 1
                    shared_k=True, q_full=q)
 
 
+def decode_v2_fp8(**kw) -> Decode:
+    """decode_v2 with an fp8 (e4m3) KV cache: the same draws, each K and V
+    sample divided by the per-tensor scale 1/56 (|x| <= 8 stays inside the
+    e4m3 range; larger samples clip to the +-448 codes) and rounded to e4m3."""
+    return decode_v2(kv_dtype="fp8", **kw)
+
+
 def decode_v2(seed: int = 4, B: int = 64, H: int = 32, H_kv: int = 8, d: int = 128,
               page: int = 64, max_pages: int = 512, ctx_lo: int = 8192, ctx_hi: int = 32768,
-              depth: int = 20, ctx_len: Optional[np.ndarray] = None) -> Decode:
+              depth: int = 20, ctx_len: Optional[np.ndarray] = None, kv_dtype: str = "bf16") -> Decode:
     """V2 paged decode, bf16. Draw order: ctx_len ~ U{ctx_lo..ctx_hi}; a random
     permutation of the P = sum ceil(L_b/page) physical pages, assigned to
     (sequence, logical page) in order (unused table slots are -1); K and V pools
@@ -246,26 +309,36 @@ def decode_v2(seed: int = 4, B: int = 64, H: int = 32, H_kv: int = 8, d: int = 1
         n = int(npg[b])
         table[b, :n] = perm[pos:pos + n]
         pos += n
-    k_cache = np.empty((P, H_kv, page, d), np.uint16)
-    v_cache = np.empty((P, H_kv, page, d), np.uint16)
+    fp8 = kv_dtype == "fp8"
+    kv_scale = 1.0 / 56.0
+    if fp8:
+        enc = lambda x: f32_to_fp8(np.clip(x / np.float32(kv_scale), -FP8_MAX, FP8_MAX))
+    else:
+        enc = f32_to_bf16
+    k_cache = np.empty((P, H_kv, page, d), np.uint8 if fp8 else np.uint16)
+    v_cache = np.empty((P, H_kv, page, d), np.uint8 if fp8 else np.uint16)
     chunk = max(1, (1 << 24) // (H_kv * page * d))
     for s in range(0, P, chunk):
         e = min(P, s + chunk)
-        k_cache[s:e] = f32_to_bf16(_normal(rng, (e - s, H_kv, page, d)))
+        k_cache[s:e] = enc(_normal(rng, (e - s, H_kv, page, d)))
     for s in range(0, P, chunk):
         e = min(P, s + chunk)
-        v_cache[s:e] = f32_to_bf16(_normal(rng, (e - s, H_kv, page, d)))
+        v_cache[s:e] = enc(_normal(rng, (e - s, H_kv, page, d)))
     q = f32_to_bf16(_normal(rng, (B, 2 * H, d), 1.0 / math.sqrt(2.0)))
     lq1, lk1, lq2, lk2 = _lambda_vectors(rng, H, d)
-    return Decode("decode_v2", "bf16", B, H, H_kv, d, d, page, max_pages, P,
-                  q[:, 0::2], q[:, 1::2], k_cache, k_cache, v_cache, table, ctx_len,
-                  lq1, lk1, lq2, lk2, depth=depth, norm=False, gamma=None, q_full=q)
+    return Decode("decode_v2_fp8" if fp8 else "decode_v2", "bf16", B, H, H_kv, d, d, page, max_pages,
+                  P, q[:, 0::2], q[:, 1::2], k_cache, k_cache, v_cache, table, ctx_len,
+                  lq1, lk1, lq2, lk2, depth=depth, norm=False, gamma=None, q_full=q,
+                  kv_dtype=kv_dtype, k_scale=kv_scale if fp8 else 1.0,
+                  v_scale=kv_scale if fp8 else 1.0)
 
 
 def decode_v1(seed: int = 6, B: int = 64, H: int = 32, H_kv: int = 8, d_qk: int = 64,
               d_v: int = 128, page: int = 64, max_pages: int = 512, ctx_lo: int = 8192,
-              ctx_hi: int = 32768, depth: int = 12, ctx_len: Optional[np.ndarray] = None) -> Decode:
-    """V1 paged decode, bf16: the V2 decode's shape family with the V1 head
+              ctx_hi: int = 32768, depth: int = 12, ctx_len: Optional[np.ndarray] = None,
+              kv_dtype: str = "bf16") -> Decode:
+    """V1 paged decode, bf16 (kv_dtype "fp8": the pools' samples divided by the
+    per-tensor scale 1/112 and rounded to e4m3 codes): the V2 decode's shape family with the V1 head
     split (d_qk 64 per branch, separate K1 and K2 caches, one V cache of width
     128) and the V1 norm. Draw order: ctx_len ~ U{ctx_lo..ctx_hi}; a random
     permutation of the P = sum ceil(L_b/page) physical pages assigned to
@@ -291,12 +364,19 @@ def decode_v1(seed: int = 6, B: int = 64, H: int = 32, H_kv: int = 8, d_qk: int 
         table[b, :n] = perm[pos:pos + n]
         pos += n
 
+    fp8 = kv_dtype == "fp8"
+    kv_scale = 1.0 / 112.0
+
     def pool(d):
-        out = np.empty((P, H_kv, page, d), np.uint16)
+        out = np.empty((P, H_kv, page, d), np.uint8 if fp8 else np.uint16)
         chunk = max(1, (1 << 24) // (H_kv * page * d))
         for s in range(0, P, chunk):
             e = min(P, s + chunk)
-            out[s:e] = f32_to_bf16(_normal(rng, (e - s, H_kv, page, d), 0.5))
+            x = _normal(rng, (e - s, H_kv, page, d), 0.5)
+            if fp8:
+                out[s:e] = f32_to_fp8(np.clip(x / np.float32(kv_scale), -FP8_MAX, FP8_MAX))
+            else:
+                out[s:e] = f32_to_bf16(x)
         return out
 
     k1_cache, k2_cache, v_cache = pool(d_qk), pool(d_qk), pool(d_v)
@@ -304,9 +384,11 @@ def decode_v1(seed: int = 6, B: int = 64, H: int = 32, H_kv: int = 8, d_qk: int 
     q2 = f32_to_bf16(_normal(rng, (B, H, d_qk), 0.5))
     lq1, lk1, lq2, lk2 = _lambda_vectors(rng, H, d_qk)
     gamma = rng.uniform(0.9, 1.1, size=(H, d_v)).astype(np.float32)
-    return Decode("decode_v1", "bf16", B, H, H_kv, d_qk, d_v, page, max_pages, P,
-                  q1, q2, k1_cache, k2_cache, v_cache, table, ctx_len,
-                  lq1, lk1, lq2, lk2, depth=depth, norm=True, gamma=gamma, shared_k=False)
+    return Decode("decode_v1_fp8" if fp8 else "decode_v1", "bf16", B, H, H_kv, d_qk, d_v, page,
+                  max_pages, P, q1, q2, k1_cache, k2_cache, v_cache, table, ctx_len,
+                  lq1, lk1, lq2, lk2, depth=depth, norm=True, gamma=gamma, shared_k=False,
+                  kv_dtype=kv_dtype, k_scale=kv_scale if fp8 else 1.0,
+                  v_scale=kv_scale if fp8 else 1.0)
 
 
 def longctx_v1(seed: int = 5, B: int = 1, H: int = 8, N: int = 65536, d_qk: int = 64,
