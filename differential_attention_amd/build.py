@@ -27,6 +27,10 @@ PLAIN_SOURCES = ["plan.cpp"]    # host code with no HIP dependency
 
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per-source device flags: the decode loop keeps its MFMA accumulators in
+# ordinary VGPRs (its online-softmax rescale reads them with VALU ops, which
+# cannot address AGPRs), avoiding a copy of every accumulator per page slice
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -53,8 +57,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     objs = []
     for s in HIP_SOURCES:
         o = os.path.join(BUILD, s + ".o")
-        cmds.append([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS, *common, "-c",
-                     os.path.join(CSRC, s), "-o", o])
+        cmds.append([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS, *SOURCE_FLAGS.get(s, []),
+                     *common, "-c", os.path.join(CSRC, s), "-o", o])
         objs.append(o)
     for s in HOST_SOURCES:
         o = os.path.join(BUILD, s + ".o")

@@ -81,6 +81,7 @@ constexpr int kBuf = DIFFATTN_DECODE_KBUF;  // pages of K/V held in registers pe
 #define DIFFATTN_DECODE_ROUNDS 1
 #endif
 constexpr int kRounds = DIFFATTN_DECODE_ROUNDS;  // rounds of resident work-groups (library's choice)
+constexpr float kLazy = 8.0f;  // lazy-rescale threshold of the running max, log2 units
 
 struct DecodeParams {
     const __bf16 *q1, *q2;
@@ -358,22 +359,34 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                     }
                     sc = mfma16(ka, qf[kc], sc);
                 }
+                if (!(S.ok && vis >= 16 && vlo <= 0)) {  // a slice with masked tokens (wave-uniform)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (!S.ok || 4 * grp + r >= vis || 4 * grp + r < vlo) sc[r] = -INFINITY;
+                    for (int r = 0; r < 4; ++r)
+                        if (!S.ok || 4 * grp + r >= vis || 4 * grp + r < vlo) sc[r] = -INFINITY;
+                }
                 float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
                 mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
                 mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float mnew = fmaxf(m, mx * p.sc_log2);
-                const float alpha = (m == mnew) ? 1.0f : exp2_fast(m - mnew);
-                const float msub = (mnew == -INFINITY) ? 0.0f : mnew;
-                m = mnew;
+                // lazy rescale: the reference m moves only when a score exceeds it
+                // by more than kLazy (log2 units), so the weights stay <= 2^kLazy
+                // and O and l are rescaled rarely; the normalisation at the end
+                // divides by l built on the same reference, so the result is the
+                // same softmax
+                const float mxs = mx * p.sc_log2;
+                const bool grow = mxs > m + kLazy;  // false while every score is masked
+                if (__any(grow)) {                  // wave-uniform
+                    const float mnew = grow ? mxs : m;
+                    const float alpha = (m == mnew) ? 1.0f : exp2_fast(m - mnew);
+                    m = mnew;
+                    l *= alpha;
+#pragma unroll
+                    for (int dc = 0; dc < 8; ++dc) o[dc] *= alpha;
+                }
+                const float msub = (m == -INFINITY) ? 0.0f : m;
                 float pr[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(fmaf(sc[r], p.sc_log2, -msub));
-                l = l * alpha + (pr[0] + pr[1]) + (pr[2] + pr[3]);
-#pragma unroll
-                for (int dc = 0; dc < 8; ++dc) o[dc] *= alpha;
+                l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
                 const bf16x2 p01 = pack2(pr[0], pr[1]), p23 = pack2(pr[2], pr[3]);
                 const bf16x4_t pb4 = {p01[0], p01[1], p23[0], p23[1]};
                 // the V rows written above must be complete before other lanes read them
@@ -392,18 +405,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 __builtin_amdgcn_s_waitcnt(0xC07F);
             };
 
+            // every slot issues its next load unconditionally (past the chunk's
+            // end it re-reads the chunk's last page, which is in L2), so the
+            // compiler can count the loads in flight and wait for the oldest
+            // slice only, keeping kBufT - 1 slices of requests outstanding
             Slice<FP8> S[kBufT];
 #pragma unroll
-            for (int j = 0; j < kBufT; ++j)
-                if (j < np) load(S[j], j);
+            for (int j = 0; j < kBufT; ++j) load(S[j], min(j, np - 1));
             for (int k0 = 0; k0 < np; k0 += kBufT) {
 #pragma unroll
                 for (int j = 0; j < kBufT; ++j) {
                     const int k = k0 + j;
-                    if (k < np) {
-                        process(S[j], k);
-                        if (k + kBufT < np) load(S[j], k + kBufT);
-                    }
+                    if (k < np) process(S[j], k);
+                    load(S[j], min(k + kBufT, np - 1));
                 }
             }
         }
