@@ -391,7 +391,7 @@ def main():
     if args.only != "decode":
         line["value"] = F / (res["prefill_part_ms"] * 1e-3) / 1e12
         ach = F / (res["prefill_kernel_ms"] * 1e-3) / 1e12
-        line["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<64,false,true>",
+        line["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<64, false, true, false>",
                             "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": ach / BF16_PEAK_TFLOPS, "traffic": load_traffic("prefill_v1")}
     if d is not None:
