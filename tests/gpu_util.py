@@ -51,6 +51,29 @@ def check(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
     return mx
 
 
+def check_all_rows_by_head(c, out, what: str):
+    """bf16 check of every row of a prefill output [B, H, N, d_v] (numpy),
+    the oracle evaluated one (batch, head) at a time with a progress line per
+    head; max abs and relative Frobenius errors accumulate over all rows."""
+    p = c.p
+    mx, dd, rr = 0.0, 0.0, 0.0
+    for b in range(p.B):
+        for h in range(p.H):
+            rows = (b * p.H + h) * p.N + np.arange(p.N, dtype=np.int64)
+            ref = c.oracle(rows=rows)
+            got = np.asarray(out[b, h], np.float64)
+            assert np.all(np.isfinite(got)), f"{what}: non-finite output in head {h}"
+            diff = got - ref
+            mx = max(mx, float(np.abs(diff).max()))
+            dd += float((diff * diff).sum())
+            rr += float((ref * ref).sum())
+            say(f"  {what}: batch {b} head {h} done, max|d| so far {mx:.3e}")
+    fro = (dd / max(rr, 1e-300)) ** 0.5
+    say(f"  {what}: max|d| {mx:.3e} rel-fro {fro:.3e} over {out.size} elements")
+    assert mx <= BF16_MAX_ABS, f"{what}: max abs error {mx}"
+    assert fro <= BF16_REL_FRO, f"{what}: relative Frobenius error {fro}"
+
+
 class PrefillCase:
     """A workload on the device plus its oracle."""
 

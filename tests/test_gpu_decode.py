@@ -186,8 +186,7 @@ def test_decode_v2_full(torch, da):
     say(f"decode_v2 full: 64 sequences, {d.num_pages} pages, context {d.ctx_len.min()}..{d.ctx_len.max()}")
     c = DecodeCase(d, torch, da)
     out = c.run().float().cpu().numpy()
-    seqs = np.array([0, 7, int(np.argmax(d.ctx_len)), int(np.argmin(d.ctx_len)), 33, 63])
-    check(out[seqs], c.oracle(seqs=seqs), "bf16", "decode_v2 sampled sequences")
+    check(out, c.oracle(), "bf16", "decode_v2 all sequences and heads")
 
 
 # ---- V1 form: d_qk 64, separate K1 and K2 caches, value width 128, RMS norm
@@ -254,8 +253,7 @@ def test_decode_v1_full(torch, da):
     say(f"decode_v1 full: 64 sequences, {d.num_pages} pages, context {d.ctx_len.min()}..{d.ctx_len.max()}")
     c = DecodeCase(d, torch, da)
     out = c.run().float().cpu().numpy()
-    seqs = np.array([0, 5, int(np.argmax(d.ctx_len)), int(np.argmin(d.ctx_len)), 40, 63])
-    check(out[seqs], c.oracle(seqs=seqs), "bf16", "decode_v1 sampled sequences")
+    check(out, c.oracle(), "bf16", "decode_v1 all sequences and heads")
 
 
 # ---- causal sliding window: the query sees its last W tokens
@@ -379,5 +377,4 @@ def test_decode_v2_fp8_full(torch, da):
     say(f"decode_v2_fp8 full: 64 sequences, {d.num_pages} pages")
     c = DecodeCase(d, torch, da)
     out = c.run().float().cpu().numpy()
-    seqs = np.array([0, 7, int(np.argmax(d.ctx_len)), int(np.argmin(d.ctx_len)), 33, 63])
-    check(out[seqs], c.oracle(seqs=seqs), "bf16", "decode_v2_fp8 sampled sequences")
+    check(out, c.oracle(), "bf16", "decode_v2_fp8 all sequences and heads")

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import (PrefillCase, check, dev, gather_rows, sampled_rows, say, to_dev)
+from gpu_util import (PrefillCase, check, check_all_rows_by_head, dev, gather_rows, sampled_rows, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -153,13 +153,12 @@ def test_causality_and_determinism(torch, da):
 # ---------------------------------------------------------------- full-size workloads
 
 def test_prefill_v1_full(torch, da):
+    # every row of every head (the oracle needs a few seconds for all 131072)
     p = W.prefill_v1()
     c = PrefillCase(p)
-    say("prefill_v1 full: B 2, H 16, N 4096, d_qk 64, d_v 128, causal, RMS")
-    out = c.run()
-    torch.cuda.synchronize()
-    rows = sampled_rows(p.B, p.H, p.N, seed=21)
-    check(gather_rows(out, rows, p.H, p.N), c.oracle(rows=rows), "bf16", "prefill_v1 sampled rows")
+    say("prefill_v1 full: B 2, H 16, N 4096, d_qk 64, d_v 128, causal, RMS; all rows")
+    out = c.run().float().cpu().numpy()
+    check(out, c.oracle(), "bf16", "prefill_v1 all rows")
 
 
 def test_prefill_v2_full(torch, da):
@@ -247,3 +246,25 @@ def test_fp32_group_norm(torch, da):
     p.norm = "group"
     c = PrefillCase(p)
     check(c.run().cpu().numpy(), c.oracle(), "f32", "f32 GroupNorm")
+
+
+# ---------------------------------------------------------------- all rows of the largest workloads
+# (minutes of oracle time each: run with --runslow)
+
+
+@pytest.mark.slow
+def test_prefill_v2_all_rows(torch, da):
+    p = W.prefill_v2()
+    c = PrefillCase(p)
+    say("prefill_v2 full: all 524288 rows against the oracle")
+    out = c.run().float().cpu().numpy()
+    check_all_rows_by_head(c, out, "prefill_v2 all rows")
+
+
+@pytest.mark.slow
+def test_longctx_v1_all_rows(torch, da):
+    p = W.longctx_v1()
+    c = PrefillCase(p)
+    say("longctx_v1 full: all 524288 rows against the oracle")
+    out = c.run().float().cpu().numpy()
+    check_all_rows_by_head(c, out, "longctx_v1 all rows")
