@@ -31,7 +31,9 @@
 //                       dK^T += Q^T dS (Q^T and dy^T by transposing reads)
 //  bwd_finalize_kernel  sums the partials per head (fixed order: deterministic)
 // Masks as the forward: causal j <= i, window j >= i - W + 1, rows and keys
-// past N. Tiles use the forward's LDS layouts (tiles.hpp).
+// past N. Tiles have the forward's LDS shapes, with the swizzles that keep
+// both row and transposed reads free of bank conflicts (tiles.hpp), since
+// every backward tile is read both ways.
 #include "launch.hpp"
 #include "tiles.hpp"
 
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     const int nsub = wrow0 < p.N ? (wend + 31) / 32 : 0;
 
     static_assert(T::kBlocks % NW == 0, "stage blocks must divide among the waves");
-    auto issue_tile = [&](int t, unsigned char *base) {
+    auto issue_tile = [&](int t, unsigned char *base) DA_INLINE {
         const int key0 = t * kBN;
 #pragma unroll
         for (int i = 0; i < T::kBlocks / NW; ++i) {
@@ -222,14 +224,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
                 const int kt = blk / (T::kKBytes / 1024);
                 const int kblk = blk % (T::kKBytes / 1024);
                 const int r = kblk * T::kRowsPerKBlock + lane / T::kKCh;
-                const int col = 8 * ((lane % T::kKCh) ^ k_swz<DQK>(r));
+                const int col = 8 * ((lane % T::kKCh) ^ bk_swz<DQK>(r));
                 const int key = min(key0 + r, p.N - 1);
                 const __bf16 *src = (kt ? kb2 + (int64_t)key * sk2n : kb1 + (int64_t)key * sk1n) + col;
                 __builtin_amdgcn_global_load_lds(src, (lds_void *)(base + blk * 1024), 16, 0, 0);
             } else {
                 const int vblk = blk - T::kKBlocks;
                 const int r = vblk * 4 + (lane >> 4);
-                const int col = 8 * ((lane & 15) ^ v_swz(r));
+                const int col = 8 * ((lane & 15) ^ bv_swz(r));
                 const int key = min(key0 + r, p.N - 1);
                 __builtin_amdgcn_global_load_lds(vb + (int64_t)key * svn + col, (lds_void *)(base + blk * 1024), 16,
                                                  0, 0);
@@ -243,21 +245,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     const int krow = perm_key(l32);
     const int kt_off = SHARED_K ? 0 : br * T::kKBytes;
 
-    auto step = [&](const unsigned char *base, int sb, bool mask, int lim, int lo) {
+    auto step = [&](const unsigned char *base, int sb, bool mask, int lim, int lo) DA_INLINE {
         const unsigned char *kt = base + kt_off;
         const unsigned char *vt = base + T::kNK * T::kKBytes;
         const int r0 = 32 * sb + krow;
         bf16x8 kf[KC];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
-            kf[kc] = as_bf16x8(*(const uint4 *)(kt + r0 * (2 * DQK) + 16 * ((2 * kc + hh) ^ k_swz<DQK>(r0))));
+            kf[kc] = as_bf16x8(*(const uint4 *)(kt + r0 * (2 * DQK) + 16 * ((2 * kc + hh) ^ bk_swz<DQK>(r0))));
         f32x16 s = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) s = mfma32(kf[kc], qf[kc], s);
         f32x16 gq = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc)
-            gq = mfma32(as_bf16x8(*(const uint4 *)(vt + r0 * 256 + 16 * ((2 * kc + hh) ^ v_swz(r0)))), df[kc], gq);
+            gq = mfma32(as_bf16x8(*(const uint4 *)(vt + r0 * 256 + 16 * ((2 * kc + hh) ^ bv_swz(r0)))), df[kc], gq);
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -276,10 +278,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int dc = 0; dc < DQK / 32; ++dc)
-                dq[dc] = mfma32(tr_frag(kt, lane, 2 * DQK, SwzK<DQK>(), sb, t, dc), pb[t], dq[dc]);
+                dq[dc] = mfma32(tr_frag(kt, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), pb[t], dq[dc]);
     };
 
-    auto tile_body = [&](const unsigned char *base, int t) {
+    auto tile_body = [&](const unsigned char *base, int t) DA_INLINE {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int j = 2 * t + sb;
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int nt = qhi > qlo ? (qhi + kBN - 1) / kBN - tlo : 0;  // query tiles per head
     const int total = nt * p.group;                                // (head, tile) pairs
 
-    auto issue_tile = [&](int x, unsigned char *base) {
+    auto issue_tile = [&](int x, unsigned char *base) DA_INLINE {
         const int hg = x / nt, t = tlo + x - hg * nt;
         const int h = g * p.group + hg;
         const int r0 = t * kBN;
@@ -385,14 +387,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
                 const int qt = blk / (kQBytes / 1024);
                 const int qbk = blk % (kQBytes / 1024);
                 const int r = qbk * kRowsPerQBlock + lane / kQCh;
-                const int col = 8 * ((lane % kQCh) ^ k_swz<DQK>(r));
+                const int col = 8 * ((lane % kQCh) ^ bk_swz<DQK>(r));
                 const int q = min(r0 + r, p.N - 1);
                 const __bf16 *src = (qt ? qb2 + (int64_t)q * p.sq2[2] : qb1 + (int64_t)q * p.sq1[2]) + col;
                 __builtin_amdgcn_global_load_lds(src, (lds_void *)(base + blk * 1024), 16, 0, 0);
             } else {
                 const int dbk = blk - kQBlocks;
                 const int r = dbk * 4 + (lane >> 4);
-                const int col = 8 * ((lane & 15) ^ v_swz(r));
+                const int col = 8 * ((lane & 15) ^ bv_swz(r));
                 const int q = min(r0 + r, p.N - 1);
                 __builtin_amdgcn_global_load_lds(db + (int64_t)q * kDV + col, (lds_void *)(base + blk * 1024), 16, 0,
                                                  0);
@@ -418,7 +420,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int qrow = perm_key(l32);
 
     // one 32-row query sub-block of the tile at `base` (query rows qb .. qb+31)
-    auto step = [&](const unsigned char *base, int sb, int qb, float lamh, bool mask) {
+    auto step = [&](const unsigned char *base, int sb, int qb, float lamh, bool mask) DA_INLINE {
         const unsigned char *t1 = base;
         const unsigned char *t2 = base + kQBytes;
         const unsigned char *td = base + 2 * kQBytes;
@@ -427,13 +429,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         f32x16 s1 = f32x16{}, s2 = f32x16{}, gq = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            const int off = r0 * (2 * DQK) + 16 * ((2 * kc + hh) ^ k_swz<DQK>(r0));
+            const int off = r0 * (2 * DQK) + 16 * ((2 * kc + hh) ^ bk_swz<DQK>(r0));
             s1 = mfma32(as_bf16x8(*(const uint4 *)(t1 + off)), kf1[kc], s1);
             s2 = mfma32(as_bf16x8(*(const uint4 *)(t2 + off)), kf2[kc], s2);
         }
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc)
-            gq = mfma32(as_bf16x8(*(const uint4 *)(td + r0 * 256 + 16 * ((2 * kc + hh) ^ v_swz(r0)))), vf[kc], gq);
+            gq = mfma32(as_bf16x8(*(const uint4 *)(td + r0 * 256 + 16 * ((2 * kc + hh) ^ bv_swz(r0)))), vf[kc], gq);
         // register r holds query row 32 sb + key_of_reg(r) + 8 hh of the tile
         float pw[16], d1[16], d2[16];
 #pragma unroll
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
                 d2[r] = -lamh * p2 * (gq[r] - D2[e]);
             }
         }
-        auto pack16 = [](const float *x, bf16x8 *out) {
+        auto pack16 = [](const float *x, bf16x8 *out) DA_INLINE {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const bf16x2 a = pack2(x[8 * t + 0], x[8 * t + 1]), c = pack2(x[8 * t + 2], x[8 * t + 3]);
@@ -478,19 +480,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int dc = 0; dc < 4; ++dc) dva[dc] = mfma32(tr_frag(td, lane, 256, SwzV(), sb, t, dc), wb[t], dva[dc]);
+            for (int dc = 0; dc < 4; ++dc) dva[dc] = mfma32(tr_frag(td, lane, 256, BSwzV(), sb, t, dc), wb[t], dva[dc]);
 #pragma unroll
             for (int dc = 0; dc < DQK / 32; ++dc) {
-                dk1a[dc] = mfma32(tr_frag(t1, lane, 2 * DQK, SwzK<DQK>(), sb, t, dc), s1b[t], dk1a[dc]);
+                dk1a[dc] = mfma32(tr_frag(t1, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), s1b[t], dk1a[dc]);
                 if (SHARED_K)
-                    dk1a[dc] = mfma32(tr_frag(t2, lane, 2 * DQK, SwzK<DQK>(), sb, t, dc), s2b[t], dk1a[dc]);
+                    dk1a[dc] = mfma32(tr_frag(t2, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), s2b[t], dk1a[dc]);
                 else
-                    dk2a[dc] = mfma32(tr_frag(t2, lane, 2 * DQK, SwzK<DQK>(), sb, t, dc), s2b[t], dk2a[dc]);
+                    dk2a[dc] = mfma32(tr_frag(t2, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), s2b[t], dk2a[dc]);
             }
         }
     };
 
-    auto tile_body = [&](const unsigned char *base, int x) {
+    auto tile_body = [&](const unsigned char *base, int x) DA_INLINE {
         const int hg = x / nt, t = tlo + x - hg * nt;
         const float lamh = p.lambda[g * p.group + hg];
 #pragma unroll

@@ -17,6 +17,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Lambdas inside the kernels capture the kernel's state by reference; one
+// left out of line would move that state (parameters, accumulator arrays) to
+// scratch memory, so every such lambda is marked always-inline.
+#define DA_INLINE __attribute__((always_inline))
+
 namespace da {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

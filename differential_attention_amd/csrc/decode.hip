@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         for (int c0 = p0; c0 < p1; c0 += 64) {
             const int np = min(64, p1 - c0);
             const int ids = lane < np ? table[c0 + lane] : 0;
-            auto load = [&](Slice<FP8> &S, int k) {
+            auto load = [&](Slice<FP8> &S, int k) DA_INLINE {
                 int phys = __builtin_amdgcn_readlane(ids, k);
                 S.ok = phys >= 0 && phys < p.num_pages;
                 bad_page |= !S.ok;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 }
             };
 
-            auto process = [&](const Slice<FP8> &S, int k) {
+            auto process = [&](const Slice<FP8> &S, int k) DA_INLINE {
                 const int pg = fp + c0 + k;                   // page index in the sequence
                 const int vis = L - pg * kPage - 16 * wave;   // rows >= vis are past the end
                 const int vlo = t0 - pg * kPage - 16 * wave;  // rows < vlo are before the window

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     // hold the K tile(s), the rest the V tile. Slot -> (row, physical chunk)
     // -> logical chunk through the row's swizzle.
     static_assert(T::kBlocks % NW == 0, "stage blocks must divide among the waves");
-    auto issue_tile = [&](int t, unsigned char *base) {
+    auto issue_tile = [&](int t, unsigned char *base) DA_INLINE {
         const int key0 = t * kBN;
 #pragma unroll
         for (int i = 0; i < T::kBlocks / NW; ++i) {
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 
     // byte offset of this lane's K-operand chunk for k step kc, sub-block sb
     const int krow = perm_key(l32);
-    auto k_addr = [&](int sb, int kc) {
+    auto k_addr = [&](int sb, int kc) DA_INLINE {
         const int row = 32 * sb + krow;
         const int c = (2 * kc + hh) ^ k_swz<DQK>(row);
         return row * (2 * DQK) + 16 * c;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     // (sub-block sb, k step t, dv block dc, half)
     const int vi = lane & 15;  // lane inside its 16-lane group
     const int vdv0 = 16 * ((lane >> 4) & 1);
-    auto v_addr = [&](int sb, int t, int dc, int half) {
+    auto v_addr = [&](int sb, int t, int dc, int half) DA_INLINE {
         const int row = 32 * sb + 16 * t + 8 * hh + 4 * half + (vi >> 2);
         const int col = 32 * dc + vdv0 + 4 * (vi & 3);
         const int c = (col >> 3) ^ v_swz(row);
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     // one branch of one sub-block: scores, online softmax (reference max moved
     // lazily), bf16 probabilities for the two 16-key steps
     auto softmax_branch = [&](const unsigned char *kt, const bf16x8 *q, int sb, bool mask, int lim, int lo, float &mr,
-                              float &lr, f32x16 *orr, bf16x8 &pb0, bf16x8 &pb1) {
+                              float &lr, f32x16 *orr, bf16x8 &pb0, bf16x8 &pb1) DA_INLINE {
         f32x16 s = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) s = mfma32(as_bf16x8(*(const uint4 *)(kt + k_addr(sb, kc))), q[kc], s);
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         pb1 = bf16x8{pp[4][0], pp[4][1], pp[5][0], pp[5][1], pp[6][0], pp[6][1], pp[7][0], pp[7][1]};
     };
 
-    auto step = [&](const unsigned char *base, int sb, bool mask, int lim, int lo) {
+    auto step = [&](const unsigned char *base, int sb, bool mask, int lim, int lo) DA_INLINE {
         const unsigned char *vt = base + T::kNK * T::kKBytes;
         bf16x8 pb[NBR][2];
 #pragma unroll
@@ -289,9 +289,9 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         // dv block is outer (the two branches' products already alternate), which
         // keeps the register footprint of the two-branch wave within budget.
         constexpr bool kStepOuter = NBR == 1;
-        auto t_of = [](int i) { return kStepOuter ? (i >> 2) : (i & 1); };
-        auto dc_of = [](int i) { return kStepOuter ? (i & 3) : (i >> 1); };
-        auto vfrag = [&](int i) {
+        auto t_of = [](int i) DA_INLINE { return kStepOuter ? (i >> 2) : (i & 1); };
+        auto dc_of = [](int i) DA_INLINE { return kStepOuter ? (i & 3) : (i >> 1); };
+        auto vfrag = [&](int i) DA_INLINE {
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, t_of(i), dc_of(i), 0)));
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, t_of(i), dc_of(i), 1)));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     };
 
     // ---- the key sweep: even tiles in stage 0, odd tiles in stage 1
-    auto tile_body = [&](const unsigned char *base, int t) {
+    auto tile_body = [&](const unsigned char *base, int t) DA_INLINE {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int j = 2 * t + sb;

@@ -29,24 +29,51 @@ __device__ __forceinline__ int perm_key(int m) { return (m & 0x13) | ((m & 4) <<
 // register r of an accumulator whose A-operand rows were permuted as above.
 __device__ __forceinline__ constexpr int key_of_reg(int r) { return 16 * ((r >> 3) & 1) + 4 * ((r >> 2) & 1) + (r & 3); }
 
-// XOR swizzle of the 16-byte chunk index inside a row of width DQK
-// (row bytes 2 * DQK): keeps the 16 lanes of one ds_read_b128 pass on
-// distinct banks.
+// XOR swizzles of the 16-byte chunk index inside a tile row.
+//
+// Forward tiles are read one way each: K tiles by rows (ds_read_b128, 16
+// lanes per pass reading one chunk of 16 different rows of an aligned 16-row
+// block) and V tiles transposed (ds_read_b64_tr_b16, 32 lanes per pass reading
+// 4 consecutive chunks of 4 consecutive rows that start at a multiple of 4).
+// These swizzles keep each pattern on distinct banks and fold into immediate
+// LDS offsets (few address registers):
 template <int DQK>
 __device__ __forceinline__ int k_swz(int row) {
-    return DQK == 128 ? (row & 15) : ((row >> 1) & 7);
+    return DQK == 128 ? (row & 15) : ((row >> 1) & 7);  // row reads
 }
-// XOR swizzle of the chunk index inside a 256-byte row: the four rows read
-// by one ds_read_b64_tr_b16 pass land on distinct banks.
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }  // transposed reads
 
-// the two swizzles as function objects (for tr_frag)
+// Backward tiles (K, Q, V, output gradient) are read both ways. Both passes
+// touch every bank once when:
+//  * 256-byte rows (d 128, and the value / output-gradient tiles): the swizzle
+//    is a bijection of the row's 4 low bits (row reads) whose bits 2-3 differ
+//    across 4 consecutive rows (transposed reads): 4 (row & 3) + ((row >> 2) & 3).
+//  * 128-byte rows (d 64; two rows per 256-byte bank period): a bijection of
+//    row bits 1-3 for either row parity (row reads) that differs in bit 2
+//    between rows r and r + 2 of a 4-row group (transposed reads):
+//    4 ((row >> 1) & 1) + ((row >> 2) & 3).
+__device__ __forceinline__ int swz256(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int swz128(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+template <int DQK>
+__device__ __forceinline__ int bk_swz(int row) {
+    return DQK == 128 ? swz256(row) : swz128(row);
+}
+__device__ __forceinline__ int bv_swz(int row) { return swz256(row); }
+
+// the swizzles as function objects (for tr_frag)
 template <int DQK>
 struct SwzK {
     __device__ __forceinline__ int operator()(int row) const { return k_swz<DQK>(row); }
 };
 struct SwzV {
     __device__ __forceinline__ int operator()(int row) const { return v_swz(row); }
+};
+template <int DQK>
+struct BSwzK {
+    __device__ __forceinline__ int operator()(int row) const { return bk_swz<DQK>(row); }
+};
+struct BSwzV {
+    __device__ __forceinline__ int operator()(int row) const { return bv_swz(row); }
 };
 
 __device__ __forceinline__ uint4 ldg16(const __bf16 *p) { return *(const uint4 *)p; }
