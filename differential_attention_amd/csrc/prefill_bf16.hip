@@ -324,18 +324,42 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
             }
         }
     };
-    // tiles tlo, tlo+1, ... alternate between stage 0 and stage 1
-    if (tlo < ntiles) issue_tile(tlo, st0);
-    for (int t = tlo; t < ntiles; t += 2) {
-        wait_vmem_all();
-        __syncthreads();  // tile t visible to all waves; tile t-1 no longer read
-        if (t + 1 < ntiles) issue_tile(t + 1, st1);
-        tile_body(st0, t);
-        if (t + 1 >= ntiles) break;
-        wait_vmem_all();
-        __syncthreads();  // tile t+1 visible to all waves; tile t no longer read
-        if (t + 2 < ntiles) issue_tile(t + 2, st0);
-        tile_body(st1, t + 1);
+    // Without a window, a wave masks only its last sub-block (its diagonal, or
+    // the ragged end of the keys). The sweep then runs the unmasked steps alone
+    // and that one masked step follows it: a mask test inside the sweep would
+    // let the compiler merge the two variants of a step and evaluate the mask
+    // for every sub-block. The last sub-block always lies in one of the last
+    // two tiles, which are still in their stages when the sweep ends.
+    auto tile_body_open = [&](const unsigned char *base, int t) DA_INLINE {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+            if (2 * t + sb < nsub - 1) step(base, sb, false, 0, 0);
+    };
+    auto sweep = [&](auto body) DA_INLINE {
+        // tiles tlo, tlo+1, ... alternate between stage 0 and stage 1
+        if (tlo < ntiles) issue_tile(tlo, st0);
+        for (int t = tlo; t < ntiles; t += 2) {
+            wait_vmem_all();
+            __syncthreads();  // tile t visible to all waves; tile t-1 no longer read
+            if (t + 1 < ntiles) issue_tile(t + 1, st1);
+            body(st0, t);
+            if (t + 1 >= ntiles) break;
+            wait_vmem_all();
+            __syncthreads();  // tile t+1 visible to all waves; tile t no longer read
+            if (t + 2 < ntiles) issue_tile(t + 2, st0);
+            body(st1, t + 1);
+        }
+    };
+    if constexpr (WIN) {
+        sweep(tile_body);
+    } else {
+        sweep(tile_body_open);
+        if (nsub > 0) {
+            const int j = nsub - 1, t = j >> 1;
+            const int key0 = j * 32 + 8 * hh;
+            const int lim = (p.causal ? min(myrow + 1, p.N) : p.N) - key0;
+            step(((t - tlo) & 1) ? st1 : st0, j & 1, true, lim, INT_MIN / 2);
+        }
     }
 
     // ---- epilogue: y = O1 / l1 - lambda O2 / l2 (then the V1 norm), bf16 store
