@@ -350,16 +350,50 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
             body(st1, t + 1);
         }
     };
+    // the masked last sub-block, after the sweep (the sweep skipped it)
+    auto last_step = [&]() DA_INLINE {
+        const int j = nsub - 1, t = j >> 1;
+        const int key0 = j * 32 + 8 * hh;
+        const int lim = (p.causal ? min(myrow + 1, p.N) : p.N) - key0;
+        const int lo = WIN ? myrow - win + 1 - key0 : INT_MIN / 2;
+        step(((t - tlo) & 1) ? st1 : st0, j & 1, true, lim, lo);
+    };
     if constexpr (WIN) {
-        sweep(tile_body);
+        // With a window, the sub-blocks below a wave's window start (those
+        // before jmask) also need a mask; they all lie in the first 4 tiles,
+        // so those run with the general body and the rest of the sweep is
+        // open, in two loops (no mask test inside the second).
+        const int tsplit = min(ntiles, tlo + 4);  // tsplit - tlo even unless tsplit == ntiles
+        if (tlo < ntiles) issue_tile(tlo, st0);
+        int t = tlo;
+        for (; t < tsplit; t += 2) {
+            wait_vmem_all();
+            __syncthreads();
+            if (t + 1 < ntiles) issue_tile(t + 1, st1);
+            tile_body(st0, t);
+            if (t + 1 < ntiles) {
+                wait_vmem_all();
+                __syncthreads();
+                if (t + 2 < ntiles) issue_tile(t + 2, st0);
+                tile_body(st1, t + 1);
+            }
+        }
+        for (; t < ntiles; t += 2) {  // starts in stage 0: t - tlo is even here
+            wait_vmem_all();
+            __syncthreads();
+            if (t + 1 < ntiles) issue_tile(t + 1, st1);
+            tile_body_open(st0, t);
+            if (t + 1 >= ntiles) break;
+            wait_vmem_all();
+            __syncthreads();
+            if (t + 2 < ntiles) issue_tile(t + 2, st0);
+            tile_body_open(st1, t + 1);
+        }
+        // the general body already ran the last sub-block if it lies in the first tiles
+        if (nsub > 0 && nsub - 1 >= 2 * tsplit) last_step();
     } else {
         sweep(tile_body_open);
-        if (nsub > 0) {
-            const int j = nsub - 1, t = j >> 1;
-            const int key0 = j * 32 + 8 * hh;
-            const int lim = (p.causal ? min(myrow + 1, p.N) : p.N) - key0;
-            step(((t - tlo) & 1) ? st1 : st0, j & 1, true, lim, INT_MIN / 2);
-        }
+        if (nsub > 0) last_step();
     }
 
     // ---- epilogue: y = O1 / l1 - lambda O2 / l2 (then the V1 norm), bf16 store
