@@ -260,13 +260,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc)
             gq = mfma32(as_bf16x8(*(const uint4 *)(vt + r0 * 256 + 16 * ((2 * kc + hh) ^ bv_swz(r0)))), df[kc], gq);
-        float ds[16];
+        float pr[16], ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float pr = exp2_fast(fmaf(s[r], p.sc_log2, -lse2));
-            if (mask && (key_of_reg(r) >= lim || key_of_reg(r) < lo)) pr = 0.0f;
-            ds[r] = w * pr * (gq[r] - dtr);
+        for (int r = 0; r < 16; ++r) pr[r] = exp2_fast(fmaf(s[r], p.sc_log2, -lse2));
+        if (mask) {
+            // an opaque statement keeps this a branch taken by the few masked
+            // sub-blocks, instead of per-element selects evaluated for all
+            asm volatile("");
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (key_of_reg(r) >= lim || key_of_reg(r) < lo) pr[r] = 0.0f;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = w * pr[r] * (gq[r] - dtr);
         bf16x8 pb[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         for (int kc = 0; kc < 8; ++kc)
             gq = mfma32(as_bf16x8(*(const uint4 *)(td + r0 * 256 + 16 * ((2 * kc + hh) ^ bv_swz(r0)))), vf[kc], gq);
         // register r holds query row 32 sb + key_of_reg(r) + 8 hh of the tile
-        float pw[16], d1[16], d2[16];
+        float p1[16], p2[16], D1[16], D2[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int rr = 32 * sb + key_of_reg(4 * r4) + 8 * hh;  // 4 consecutive rows
@@ -446,24 +452,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             const float4 t1v = *(const float4 *)(stat + 128 + rr);
             const float4 t2v = *(const float4 *)(stat + 192 + rr);
             const float L1[4] = {l1.x, l1.y, l1.z, l1.w}, L2[4] = {l2.x, l2.y, l2.z, l2.w};
-            const float D1[4] = {t1v.x, t1v.y, t1v.z, t1v.w}, D2[4] = {t2v.x, t2v.y, t2v.z, t2v.w};
+            const float T1[4] = {t1v.x, t1v.y, t1v.z, t1v.w}, T2[4] = {t2v.x, t2v.y, t2v.z, t2v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * r4 + e;
-                float p1 = exp2_fast(fmaf(s1[r], p.sc_log2, -L1[e] * kLog2e));
-                float p2 = exp2_fast(fmaf(s2[r], p.sc_log2, -L2[e] * kLog2e));
-                if (mask) {
-                    const int q = qb + key_of_reg(r) + 8 * hh;
-                    const bool vis = q < p.N && (!p.causal || q >= mykey) && (!WIN || q - mykey < win);
-                    if (!vis) {
-                        p1 = 0.0f;
-                        p2 = 0.0f;
-                    }
-                }
-                pw[r] = p1 - lamh * p2;
-                d1[r] = p1 * (gq[r] - D1[e]);
-                d2[r] = -lamh * p2 * (gq[r] - D2[e]);
+                p1[r] = exp2_fast(fmaf(s1[r], p.sc_log2, -L1[e] * kLog2e));
+                p2[r] = exp2_fast(fmaf(s2[r], p.sc_log2, -L2[e] * kLog2e));
+                D1[r] = T1[e];
+                D2[r] = T2[e];
             }
+        }
+        if (mask) {
+            // an opaque statement keeps this a branch taken by the few masked
+            // sub-blocks, instead of per-element selects evaluated for all
+            asm volatile("");
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int q = qb + key_of_reg(r) + 8 * hh;
+                const bool vis = q < p.N && (!p.causal || q >= mykey) && (!WIN || q - mykey < win);
+                if (!vis) {
+                    p1[r] = 0.0f;
+                    p2[r] = 0.0f;
+                }
+            }
+        }
+        float pw[16], d1[16], d2[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            pw[r] = p1[r] - lamh * p2[r];
+            d1[r] = p1[r] * (gq[r] - D1[r]);
+            d2[r] = -lamh * p2[r] * (gq[r] - D2[r]);
         }
         auto pack16 = [](const float *x, bf16x8 *out) DA_INLINE {
 #pragma unroll
