@@ -432,16 +432,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         const unsigned char *td = base + 2 * kQBytes;
         const float *stat = (const float *)(base + 2 * kQBytes + kDBytes);
         const int r0 = 32 * sb + qrow;
-        f32x16 s1 = f32x16{}, s2 = f32x16{}, gq = f32x16{};
+        // the A operands of the three products are read in one batch ahead of
+        // them: with one wave per SIMD nothing else hides an LDS read's latency,
+        // so a read issued just before its product would stall every product
+        bf16x8 a1[KC], a2[KC], ad[8];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             const int off = r0 * (2 * DQK) + 16 * ((2 * kc + hh) ^ bk_swz<DQK>(r0));
-            s1 = mfma32(as_bf16x8(*(const uint4 *)(t1 + off)), kf1[kc], s1);
-            s2 = mfma32(as_bf16x8(*(const uint4 *)(t2 + off)), kf2[kc], s2);
+            a1[kc] = as_bf16x8(*(const uint4 *)(t1 + off));
+            a2[kc] = as_bf16x8(*(const uint4 *)(t2 + off));
         }
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc)
-            gq = mfma32(as_bf16x8(*(const uint4 *)(td + r0 * 256 + 16 * ((2 * kc + hh) ^ bv_swz(r0)))), vf[kc], gq);
+        for (int kc = 0; kc < 8; ++kc) ad[kc] = as_bf16x8(*(const uint4 *)(td + r0 * 256 + 16 * ((2 * kc + hh) ^ bv_swz(r0))));
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 s1 = f32x16{}, s2 = f32x16{}, gq = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            s1 = mfma32(a1[kc], kf1[kc], s1);
+            s2 = mfma32(a2[kc], kf2[kc], s2);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) gq = mfma32(ad[kc], vf[kc], gq);
         // register r holds query row 32 sb + key_of_reg(r) + 8 hh of the tile
         float p1[16], p2[16], D1[16], D2[16];
 #pragma unroll

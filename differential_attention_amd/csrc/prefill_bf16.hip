@@ -60,7 +60,6 @@ namespace da {
 
 namespace {
 
-constexpr int kBM = 128;              // query rows per work-group
 constexpr int kWM = 32;               // query rows per wave
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
@@ -68,9 +67,10 @@ constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 template <int DQK>
 struct Split {
     static constexpr bool kOn = DQK == 128;
-    static constexpr int kThreads = kOn ? 512 : 256;
+    static constexpr int kThreads = 512;
+    static constexpr int kBM = kOn ? 128 : 256;  // query rows per work-group
     static constexpr int kNBr = kOn ? 1 : 2;  // branches per wave
-    static constexpr int kMinBlocks = kOn ? 1 : 2;
+    static constexpr int kMinBlocks = 1;
 };
 
 struct Bf16Params {
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         rb = p.causal ? p.row_blocks - 1 - rank : rank;
     }
     const int g = h / p.group;
-    const int q0 = rb * kBM;
+    const int q0 = rb * S::kBM;
     const int wrow0 = q0 + rg * kWM;  // first query row of this wave
     const int myrow = wrow0 + l32;    // the query row of this lane
 
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     const __bf16 *vb = p.v + b * p.sv[0] + g * p.sv[1];
     const int64_t sk1n = p.sk1[2], sk2n = p.sk2[2], svn = p.sv[2];
 
-    const int kend = p.causal ? min(p.N, q0 + kBM) : p.N;
+    const int kend = p.causal ? min(p.N, q0 + S::kBM) : p.N;
     const int ntiles = (kend + kBN - 1) / kBN;
     // causal window W: row i sees keys i-W+1 .. i, so tiles below the work-
     // group's first row's window are never loaded, sub-blocks below this
@@ -237,6 +237,9 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) s = mfma32(as_bf16x8(*(const uint4 *)(kt + k_addr(sb, kc))), q[kc], s);
         if (mask) {
+            // an opaque statement keeps this a branch taken by the few masked
+            // sub-blocks, instead of per-element selects evaluated for all
+            asm volatile("");
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (key_of_reg(r) >= lim || key_of_reg(r) < lo) s[r] = -INFINITY;
@@ -324,76 +327,46 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
             }
         }
     };
-    // Without a window, a wave masks only its last sub-block (its diagonal, or
-    // the ragged end of the keys). The sweep then runs the unmasked steps alone
-    // and that one masked step follows it: a mask test inside the sweep would
-    // let the compiler merge the two variants of a step and evaluate the mask
-    // for every sub-block. The last sub-block always lies in one of the last
-    // two tiles, which are still in their stages when the sweep ends.
+    // The branch-split sweep runs in up to three phases, each its own loop: the general
+    // body (all masks) for the tiles holding window-start sub-blocks (the
+    // first 4 tiles, windowed kernels only), the open body (no mask code at
+    // all) through the middle, and the general body again for the last
+    // kBM / 64 tiles, which hold every wave's diagonal sub-block and the
+    // ragged end of the keys. A mask test inside one loop would let the
+    // compiler merge the two variants of a step and evaluate the mask for
+    // every sub-block. Phase boundaries sit at even tile offsets from tlo, so
+    // each phase starts in stage 0 with its first tile already issued.
     auto tile_body_open = [&](const unsigned char *base, int t) DA_INLINE {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
             if (2 * t + sb < nsub - 1) step(base, sb, false, 0, 0);
     };
-    auto sweep = [&](auto body) DA_INLINE {
-        // tiles tlo, tlo+1, ... alternate between stage 0 and stage 1
-        if (tlo < ntiles) issue_tile(tlo, st0);
-        for (int t = tlo; t < ntiles; t += 2) {
+    auto phase = [&](auto body, int t0, int t1) DA_INLINE {
+        for (int t = t0; t < t1; t += 2) {
             wait_vmem_all();
             __syncthreads();  // tile t visible to all waves; tile t-1 no longer read
             if (t + 1 < ntiles) issue_tile(t + 1, st1);
             body(st0, t);
-            if (t + 1 >= ntiles) break;
+            if (t + 1 >= t1) break;  // only the last phase can end on an odd offset
             wait_vmem_all();
             __syncthreads();  // tile t+1 visible to all waves; tile t no longer read
             if (t + 2 < ntiles) issue_tile(t + 2, st0);
             body(st1, t + 1);
         }
     };
-    // the masked last sub-block, after the sweep (the sweep skipped it)
-    auto last_step = [&]() DA_INLINE {
-        const int j = nsub - 1, t = j >> 1;
-        const int key0 = j * 32 + 8 * hh;
-        const int lim = (p.causal ? min(myrow + 1, p.N) : p.N) - key0;
-        const int lo = WIN ? myrow - win + 1 - key0 : INT_MIN / 2;
-        step(((t - tlo) & 1) ? st1 : st0, j & 1, true, lim, lo);
-    };
-    if constexpr (WIN) {
-        // With a window, the sub-blocks below a wave's window start (those
-        // before jmask) also need a mask; they all lie in the first 4 tiles,
-        // so those run with the general body and the rest of the sweep is
-        // open, in two loops (no mask test inside the second).
-        const int tsplit = min(ntiles, tlo + 4);  // tsplit - tlo even unless tsplit == ntiles
-        if (tlo < ntiles) issue_tile(tlo, st0);
-        int t = tlo;
-        for (; t < tsplit; t += 2) {
-            wait_vmem_all();
-            __syncthreads();
-            if (t + 1 < ntiles) issue_tile(t + 1, st1);
-            tile_body(st0, t);
-            if (t + 1 < ntiles) {
-                wait_vmem_all();
-                __syncthreads();
-                if (t + 2 < ntiles) issue_tile(t + 2, st0);
-                tile_body(st1, t + 1);
-            }
-        }
-        for (; t < ntiles; t += 2) {  // starts in stage 0: t - tlo is even here
-            wait_vmem_all();
-            __syncthreads();
-            if (t + 1 < ntiles) issue_tile(t + 1, st1);
-            tile_body_open(st0, t);
-            if (t + 1 >= ntiles) break;
-            wait_vmem_all();
-            __syncthreads();
-            if (t + 2 < ntiles) issue_tile(t + 2, st0);
-            tile_body_open(st1, t + 1);
-        }
-        // the general body already ran the last sub-block if it lies in the first tiles
-        if (nsub > 0 && nsub - 1 >= 2 * tsplit) last_step();
+    if (tlo < ntiles) issue_tile(tlo, st0);
+    if constexpr (S::kOn) {
+        constexpr int kTail = S::kBM / kBN;  // tiles holding the waves' diagonal sub-blocks
+        const int ta = WIN ? min(ntiles, tlo + 4) : tlo;
+        const int tb = max(ta, tlo + 2 * ((ntiles - kTail - tlo) / 2));
+        if (WIN) phase(tile_body, tlo, ta);
+        phase(tile_body_open, ta, tb);
+        phase(tile_body, tb, ntiles);
     } else {
-        sweep(tile_body_open);
-        if (nsub > 0) last_step();
+        // the two-branch kernels run one phase: the second copy of the step
+        // that separate phases need costs them more (register spills) than the
+        // guarded mask branch it saves
+        phase(tile_body, tlo, ntiles);
     }
 
     // ---- epilogue: y = O1 / l1 - lambda O2 / l2 (then the V1 norm), bf16 store
@@ -547,7 +520,8 @@ hipError_t launch_prefill_bf16(const diffattn_prefill_args &a, float scale, floa
     p.N = a.N;
     p.causal = a.causal;
     p.window = a.window;
-    p.row_blocks = (a.N + kBM - 1) / kBM;
+    const int bm = a.d_qk == 64 ? Split<64>::kBM : Split<128>::kBM;
+    p.row_blocks = (a.N + bm - 1) / bm;
     const int kv_units = a.B * a.H_kv;
     p.xcd_units = (kv_units % 8 == 0) ? kv_units / 8 : 0;
     p.sc_log2 = scale * kLog2e;
