@@ -177,3 +177,82 @@ def test_backward_group_norm(torch, da, form):
     assert np.linalg.norm(dg - ref["dgamma"]) <= 1e-2 * np.linalg.norm(ref["dgamma"])
     dl = g["dlambda"].cpu().numpy()
     assert np.all(np.abs(dl - ref["dlambda"]) <= 1e-2 * np.abs(ref["dlambda"]).max() + 1e-6)
+
+
+# ---------------------------------------------------------------- full-size gradients
+# (minutes of fp64 oracle time; run with --runslow)
+
+
+def _scalar_check(got, ref, what, tol=1e-2):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    say(f"  {what}: relative error {err:.3e}")
+    assert err <= tol, (what, err)
+
+
+@pytest.mark.slow
+def test_backward_prefill_v1_all_heads(torch, da):
+    # every head of the prefill_v1 shape, and dlambda / dgamma, which sum over
+    # all rows of all batches
+    p = W.prefill_v1()
+    c = PrefillCase(p)
+    stats = da.prefill_stats(c.q1, c.v)
+    c.run(stats=stats)
+    rng = np.random.default_rng(78)
+    dout_bits = W.f32_to_bf16(rng.standard_normal((p.B, p.H, p.N, p.d_v)).astype(np.float32))
+    g = da.backward(c.q1, c.q2, c.k1, c.k2, c.v, c.lam, stats, to_dev(dout_bits, "bf16"), depth=p.depth,
+                    norm=True, gamma=c.gamma, eps=p.eps)
+    got = {k: g[k].cpu().numpy() for k in ("dq1", "dq2", "dk1", "dk2", "dv", "dlambda", "dgamma")}
+    f = {k: p.f32(k) for k in ("q1", "q2", "k1", "k2", "v")}
+    dout = W.bf16_to_f32(dout_bits)
+    ref = {k: np.zeros_like(got[k], np.float64) for k in got}
+    for b in range(p.B):
+        for h in range(p.H):
+            sl = lambda x: x[b:b + 1, h:h + 1]
+            r = bw.prefill_backward(sl(f["q1"]), sl(f["q2"]), sl(f["k1"]), sl(f["k2"]), sl(f["v"]),
+                                    c.lam64[h:h + 1], sl(dout), depth=p.depth, causal=True, norm=True,
+                                    gamma=p.gamma[h:h + 1], eps=p.eps)
+            for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
+                ref[k][b, h] = r[k][0, 0]
+            ref["dlambda"][h] += r["dlambda"][0]
+            ref["dgamma"][h] += r["dgamma"][0]
+            say(f"  oracle head (b {b}, h {h}) done")
+    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
+        _grad_check(got[k], ref[k], f"{k} all heads")
+    _scalar_check(got["dlambda"], ref["dlambda"], "dlambda")
+    _scalar_check(got["dgamma"], ref["dgamma"], "dgamma")
+
+
+@pytest.mark.slow
+def test_backward_prefill_v2_sampled_heads(torch, da):
+    # the prefill_v2 shape (GQA, N 16384): dQ of two heads, and dK, dV of one KV
+    # head (the oracle sums its 4 output heads' contributions)
+    p = W.prefill_v2()
+    c = PrefillCase(p)
+    stats = da.prefill_stats(c.q1, c.v)
+    c.run(stats=stats)
+    rng = np.random.default_rng(79)
+    dout_bits = W.f32_to_bf16(rng.standard_normal((p.B, p.H, p.N, p.d_v)).astype(np.float32))
+    g = da.backward(c.q1, c.q2, c.k1, c.k2, c.v, c.lam, stats, to_dev(dout_bits, "bf16"), depth=p.depth,
+                    norm=False)
+    q1, q2, k, v = p.f32("q1"), p.f32("q2"), p.f32("k1"), p.f32("v")
+    dout = W.bf16_to_f32(dout_bits)
+    grp = p.H // p.H_kv
+    kvh = 5
+    heads = list(range(kvh * grp, (kvh + 1) * grp))
+    dk = np.zeros((p.N, p.d_qk))
+    dv = np.zeros((p.N, p.d_v))
+    for h in heads:
+        r = bw.prefill_backward(q1[:, h:h + 1], q2[:, h:h + 1], k[:, kvh:kvh + 1], k[:, kvh:kvh + 1],
+                                v[:, kvh:kvh + 1], c.lam64[h:h + 1], dout[:, h:h + 1], depth=p.depth,
+                                causal=True, norm=False)
+        dk += r["dk1"][0, 0] + r["dk2"][0, 0]
+        dv += r["dv"][0, 0]
+        if h in (heads[0], heads[-1]):
+            _grad_check(g["dq1"][:, h:h + 1].cpu().numpy(), r["dq1"], f"dq1 head {h}")
+            _grad_check(g["dq2"][:, h:h + 1].cpu().numpy(), r["dq2"], f"dq2 head {h}")
+        say(f"  oracle head {h} done")
+    # shared keys: the library returns the summed key gradient in dk1
+    _grad_check(g["dk1"][0, kvh].cpu().numpy(), dk, f"dk KV head {kvh}")
+    _grad_check(g["dv"][0, kvh].cpu().numpy(), dv, f"dv KV head {kvh}")
