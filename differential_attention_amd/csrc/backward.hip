@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) unsigned char st0[kStage];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[kStage];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
 
     const int U = p.B * p.H_kv;

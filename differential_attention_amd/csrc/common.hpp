@@ -24,6 +24,13 @@
 
 namespace da {
 
+// Index of the calling wave in its work-group, as a wave-uniform (scalar)
+// value. Derived from threadIdx.x alone the compiler treats it as per-lane:
+// a kernel-argument pointer chosen by wave index is then fetched with a
+// vector load, whose vmcnt wait also waits for every global -> LDS tile copy
+// the wave has in flight.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -13,15 +13,16 @@
 // max m, running sum l, unnormalised O) and the difference is taken once, in
 // fp32, in the epilogue.
 //
-// Work decomposition. A work-group owns 128 query rows of one output head,
-// in 32-row groups, one per wave or per pair of waves:
-//  * d_qk 64 (V1 shapes): 4 waves, each computes both branches of its 32 rows
-//    (256 unified registers a lane, two waves per SIMD, two work-groups a CU);
-//  * d_qk 128 (V2 shapes): 8 waves, waves 2r and 2r+1 own rows 32r..32r+31,
-//    the first for branch 1, the second for branch 2. Splitting the branches
-//    halves each wave's state (Q rows as MFMA B operands, one d_v x 32
-//    accumulator), so two waves share a SIMD where one wave holding both
-//    branches would not fit twice.
+// Work decomposition. A work-group of 8 waves owns a block of query rows of
+// one output head, in 32-row groups, one per wave or per pair of waves:
+//  * d_qk 64 (V1 shapes): 256 rows, each wave computes both branches of its
+//    32 rows (256 unified registers a lane, two waves per SIMD, one
+//    work-group a CU), so one key/value tile stream feeds 256 rows;
+//  * d_qk 128 (V2 shapes): 128 rows, waves 2r and 2r+1 own rows
+//    32r..32r+31, the first for branch 1, the second for branch 2. Splitting
+//    the branches halves each wave's state (Q rows as MFMA B operands, one
+//    d_v x 32 accumulator), so two waves share a SIMD where one wave holding
+//    both branches would not fit twice.
 //  * Key tiles of 64 keys stream HBM -> LDS with global_load_lds (16 bytes a
 //    lane, no register staging), double-buffered: the loads of tile t+1 are
 //    in flight while tile t is used. One key tile feeds both branches when
@@ -229,13 +230,17 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     };
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // one branch of one sub-block: scores, online softmax (reference max moved
-    // lazily), bf16 probabilities for the two 16-key steps
-    auto softmax_branch = [&](const unsigned char *kt, const bf16x8 *q, int sb, bool mask, int lim, int lo, float &mr,
-                              float &lr, f32x16 *orr, bf16x8 &pb0, bf16x8 &pb1) DA_INLINE {
+    // scores S^T = K Q^T of one branch for one sub-block
+    auto qk_branch = [&](const unsigned char *kt, const bf16x8 *q, int sb) DA_INLINE {
         f32x16 s = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) s = mfma32(as_bf16x8(*(const uint4 *)(kt + k_addr(sb, kc))), q[kc], s);
+        return s;
+    };
+    // online softmax of one branch's scores (reference max moved lazily), bf16
+    // probabilities for the two 16-key steps
+    auto softmax_branch = [&](f32x16 s, bool mask, int lim, int lo, float &mr, float &lr, f32x16 *orr, bf16x8 &pb0,
+                              bf16x8 &pb1) DA_INLINE {
         if (mask) {
             // an opaque statement keeps this a branch taken by the few masked
             // sub-blocks, instead of per-element selects evaluated for all
@@ -278,12 +283,15 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 
     auto step = [&](const unsigned char *base, int sb, bool mask, int lim, int lo) DA_INLINE {
         const unsigned char *vt = base + T::kNK * T::kKBytes;
+        // every branch's score products first: with two branches per wave the
+        // two product chains interleave, and the rescale test of one branch
+        // (a branch in the code) no longer sits between them
+        f32x16 sc[NBR];
+#pragma unroll
+        for (int j = 0; j < NBR; ++j) sc[j] = qk_branch(base + (SHARED_K ? 0 : (br0 + j) * T::kKBytes), qf[j], sb);
         bf16x8 pb[NBR][2];
 #pragma unroll
-        for (int j = 0; j < NBR; ++j) {
-            const unsigned char *kt = base + (SHARED_K ? 0 : (br0 + j) * T::kKBytes);
-            softmax_branch(kt, qf[j], sb, mask, lim, lo, m[j], l[j], o[j], pb[j][0], pb[j][1]);
-        }
+        for (int j = 0; j < NBR; ++j) softmax_branch(sc[j], mask, lim, lo, m[j], l[j], o[j], pb[j][0], pb[j][1]);
         // O^T += V^T P^T, one V read for every branch of the wave; the next
         // step's V operand is read while this step's products run
         // step i covers (k step t, dv block dc). With one branch per wave the k
