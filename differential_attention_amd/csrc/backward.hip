@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
     auto tile_body = [&](const unsigned char *base, int x) DA_INLINE {
         const int hg = x / nt, t = tlo + x - hg * nt;
-        const float lamh = p.lambda[g * p.group + hg];
+        const float lamh = ld_uniform(p.lambda + g * p.group + hg);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int qb = t * kBN + 32 * sb;  // first query row of the sub-block

@@ -31,6 +31,14 @@ namespace da {
 // the wave has in flight.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Load of a wave-uniform value that no kernel writes while this one runs,
+// through the constant address space: a scalar load, counted by lgkmcnt. As a
+// vector load inside a tile loop its vmcnt wait would also wait for the tile
+// copies issued before it.
+__device__ __forceinline__ float ld_uniform(const float *p) {
+    return *(const __attribute__((address_space(4))) float *)(uintptr_t)p;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
