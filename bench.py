@@ -112,6 +112,18 @@ def load_traffic(name):
     return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo gives it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(p, lam64, budget_s):
     """Oracle FLOP/s on a random sample of prefill rows (same inputs)."""
     import oracle
@@ -132,7 +144,7 @@ def cpu_baseline(p, lam64, budget_s):
     f, t = run(n)
     return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} random query rows of prefill_v1 (of {p.B * p.H * p.N}), fp64, "
-                      f"{t:.1f} s, FLOPs counted per visible key as for the GPU"}
+                      f"{t:.1f} s on {cpu_model()}, FLOPs counted per visible key as for the GPU"}
 
 
 def single_workload(args, torch, da, W, dev):
