@@ -404,7 +404,9 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     if constexpr (S::kOn) {
         // branch-2 waves hand lambda O2 / l2 to their branch-1 partner through LDS
         __syncthreads();  // every wave is done with the key tiles
-        float *xch = (float *)(rg < 2 ? st0 : st1) + (((rg & 1) * 64 + lane) * 64);  // this lane's 64 values
+        // a row group's 64 x 64 values, stored float4 by float4 with the 64 lanes'
+        // float4s of one (dc, q) contiguous, so every access is conflict-free
+        float *xch = (float *)(rg < 2 ? st0 : st1) + (rg & 1) * 64 * 64 + 4 * lane;
         if (br0) {
             const float r2 = p.lambda[h] / l[0];
 #pragma unroll
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float4 v4 = {w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
-                    *(float4 *)(xch + 16 * dc + 4 * q) = v4;
+                    *(float4 *)(xch + 256 * (4 * dc + q)) = v4;
                 }
             }
         }
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
             f32x16 w2;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float4 v4 = *(const float4 *)(xch + 16 * dc + 4 * q);
+                const float4 v4 = *(const float4 *)(xch + 256 * (4 * dc + q));
                 w2[4 * q] = v4.x;
                 w2[4 * q + 1] = v4.y;
                 w2[4 * q + 2] = v4.z;
