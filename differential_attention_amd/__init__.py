@@ -209,6 +209,28 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
+def _need(t, name: str, dtype=None, shape=None, contiguous: bool = False):
+    """Check one tensor argument before its pointer reaches the library: the
+    kernels read exactly the sizes the ABI is given, so a wrong dtype (an
+    int64 table read as int32 pairs) or shape would be read silently wrong or
+    out of bounds. Checks dtype, then shape, then layout (the device is
+    checked for all arguments together by _on_device)."""
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _on_device(**tensors):
+    """Every tensor argument (None allowed) must live in device memory."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
 def lambda_init(depth: int) -> float:
     """lambda_init(depth) = 0.8 - 0.6 exp(-0.3 (depth - 1)) (host, fp64)."""
     return float(load_library().diffattn_lambda_init(int(depth)))
@@ -224,6 +246,7 @@ def lambda_(lq1, lk1, lq2, lk2, depth: int, out=None, stream=None):
             raise ValueError("lambda vectors must be [H, d_lambda] fp32 device tensors of one shape")
     if out is None:
         out = torch.empty(H, dtype=torch.float32, device=vecs[0].device)
+    _need(out, "out", torch.float32, (H,), contiguous=True)
     rc = load_library().diffattn_lambda(*(_ptr(x) for x in vecs), H, dl, int(depth), _ptr(out),
                                         _stream(stream))
     _check(rc)
@@ -252,28 +275,37 @@ def prefill(q1, q2, k1, k2, v, lam, *, depth: int, causal: bool = True, norm: bo
     import torch
     B, H, N, dqk = q1.shape
     Hkv, dv = k1.shape[1], v.shape[3]
-    if out is None:
-        out = torch.empty((B, H, N, dv), dtype=q1.dtype, device=q1.device)
     a = PrefillArgs()
     a.dtype = _dtype_code(q1)
-    for t in (q2, k1, k2, v, out):
-        if t.dtype != q1.dtype:
-            raise TypeError("all tensors must share one dtype")
+    _need(q1, "q1")
+    _need(q2, "q2", q1.dtype, q1.shape)
+    _need(k1, "k1", q1.dtype, (B, Hkv, N, dqk))
+    _need(k2, "k2", q1.dtype, (B, Hkv, N, dqk))
+    _need(v, "v", q1.dtype, (B, Hkv, N, dv))
+    _need(lam, "lam", torch.float32, (H,), contiguous=True)
+    if norm:
+        if gamma is None:
+            raise ValueError("gamma [H, d_v] is required with a norm")
+        _need(gamma, "gamma", torch.float32, (H, dv), contiguous=True)
+    if out is not None:
+        _need(out, "out", q1.dtype, (B, H, N, dv))
+    _on_device(q1=q1, q2=q2, k1=k1, k2=k2, v=v, lam=lam, gamma=gamma if norm else None, out=out)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q1.dtype, device=q1.device)
     a.B, a.H, a.H_kv, a.N, a.d_qk, a.d_v = B, H, Hkv, N, dqk, dv
     a.q1, a.q2, a.k1, a.k2, a.v = _ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v)
     a.sq1, a.sq2 = _c_int64_3(*_strides3(q1)), _c_int64_3(*_strides3(q2))
     a.sk1, a.sk2 = _c_int64_3(*_strides3(k1)), _c_int64_3(*_strides3(k2))
     a.sv, a.so = _c_int64_3(*_strides3(v)), _c_int64_3(*_strides3(out))
-    if lam.dtype != torch.float32 or lam.numel() != H:
-        raise ValueError("lam must be an fp32 tensor of H elements")
     a.lambda_ = _ptr(lam)
     a.depth = int(depth)
     a.causal = int(bool(causal))
     a.window = int(window)
     if stats is not None:
-        for t, shape in zip(stats, ((B, H, N, dv), (B, H, N, dv), (B, H, N), (B, H, N))):
-            if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
-                raise ValueError(f"stats tensors must be contiguous fp32 of shapes {shape}")
+        for t, shape, nm in zip(stats, ((B, H, N, dv), (B, H, N, dv), (B, H, N), (B, H, N)),
+                                ("o1", "o2", "lse1", "lse2")):
+            _need(t, "stats " + nm, torch.float32, shape, contiguous=True)
+        _on_device(o1=stats[0], o2=stats[1], lse1=stats[2], lse2=stats[3])
         a.o1, a.o2, a.lse1, a.lse2 = (_ptr(t) for t in stats)
     a.scale = float(scale)
     a.norm = _norm_code(norm)
@@ -312,9 +344,22 @@ def backward(q1, q2, k1, k2, v, lam, stats, dout, *, depth: int, causal: bool = 
     a = BackwardArgs()
     a.dtype = _dtype_code(q1)
     a.B, a.H, a.H_kv, a.N, a.d_qk, a.d_v = B, H, Hkv, N, dqk, dv_
-    for t in (q2, k1, k2, v, dout):
-        if t.dtype != q1.dtype:
-            raise ValueError("all inputs must share one dtype")
+    _need(q1, "q1")
+    _need(q2, "q2", q1.dtype, q1.shape)
+    _need(k1, "k1", q1.dtype, (B, Hkv, N, dqk))
+    _need(k2, "k2", q1.dtype, (B, Hkv, N, dqk))
+    _need(v, "v", q1.dtype, (B, Hkv, N, dv_))
+    _need(dout, "dout", q1.dtype, (B, H, N, dv_))
+    _need(lam, "lam", torch.float32, (H,), contiguous=True)
+    if norm:
+        if gamma is None:
+            raise ValueError("gamma [H, d_v] is required with a norm")
+        _need(gamma, "gamma", torch.float32, (H, dv_), contiguous=True)
+    for t, shape, nm in zip(stats, ((B, H, N, dv_), (B, H, N, dv_), (B, H, N), (B, H, N)),
+                            ("o1", "o2", "lse1", "lse2")):
+        _need(t, "stats " + nm, torch.float32, shape, contiguous=True)
+    _on_device(q1=q1, q2=q2, k1=k1, k2=k2, v=v, dout=dout, lam=lam, gamma=gamma if norm else None,
+               o1=stats[0], o2=stats[1], lse1=stats[2], lse2=stats[3])
     a.q1, a.q2, a.k1, a.k2, a.v = (_ptr(t) for t in (q1, q2, k1, k2, v))
     a.sq1, a.sq2 = _c_int64_3(*_strides3(q1)), _c_int64_3(*_strides3(q2))
     a.sk1, a.sk2 = _c_int64_3(*_strides3(k1)), _c_int64_3(*_strides3(k2))
@@ -324,9 +369,6 @@ def backward(q1, q2, k1, k2, v, lam, stats, dout, *, depth: int, causal: bool = 
     a.norm = _norm_code(norm)
     a.gamma = _ptr(gamma) if norm else None
     a.eps = float(eps)
-    for t in stats:
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("stats must be contiguous fp32 tensors")
     a.o1, a.o2, a.lse1, a.lse2 = (_ptr(t) for t in stats)
     a.dout = _ptr(dout)
     a.sdo = _c_int64_3(*_strides3(dout))
@@ -345,6 +387,10 @@ def lambda_backward(lq1, lk1, lq2, lk2, dlambda, stream=None):
     """Gradients of the four [H, d_lambda] lambda vectors given dlambda [H]."""
     import torch
     H, dl = lq1.shape
+    for t, nm in zip((lq1, lk1, lq2, lk2), ("lq1", "lk1", "lq2", "lk2")):
+        _need(t, nm, torch.float32, (H, dl), contiguous=True)
+    _need(dlambda, "dlambda", torch.float32, (H,), contiguous=True)
+    _on_device(lq1=lq1, lk1=lk1, lq2=lq2, lk2=lk2, dlambda=dlambda)
     outs = [torch.empty_like(lq1) for _ in range(4)]
     _check(load_library().diffattn_lambda_backward(_ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), H, dl,
                                                    _ptr(dlambda), *(_ptr(t) for t in outs), _stream(stream)))
@@ -354,9 +400,33 @@ def lambda_backward(lq1, lk1, lq2, lk2, dlambda, stream=None):
 def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
                  scale, out, split_pages, dev_err, k2_cache=None, window=0, k_scale=1.0,
                  v_scale=1.0) -> DecodeArgs:
+    import torch
     B, H, dqk = q1.shape
     P, Hkv, page, _ = k_cache.shape
     dv = v_cache.shape[3]
+    _need(q1, "q1")
+    _need(q2, "q2", q1.dtype, q1.shape)
+    if k_cache.dtype not in (torch.bfloat16, torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"k_cache must be bf16 or fp8 e4m3 (float8_e4m3fn or uint8 codes), got {k_cache.dtype}")
+    _need(k_cache, "k_cache", shape=(P, Hkv, page, dqk), contiguous=True)
+    if k2_cache is not None:
+        _need(k2_cache, "k2_cache", k_cache.dtype, (P, Hkv, page, dqk), contiguous=True)
+    _need(v_cache, "v_cache", shape=(P, Hkv, page, dv), contiguous=True)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError(f"page_table must have shape [B={B}, max_pages], got {tuple(page_table.shape)}")
+    _need(page_table, "page_table", torch.int32, contiguous=True)
+    _need(ctx_len, "ctx_len", torch.int32, (B,), contiguous=True)
+    _need(lam, "lam", torch.float32, (H,), contiguous=True)
+    if norm:
+        if gamma is None:
+            raise ValueError("gamma [H, d_v] is required with a norm")
+        _need(gamma, "gamma", torch.float32, (H, dv), contiguous=True)
+    if out is not None:
+        _need(out, "out", q1.dtype, (B, H, dv))
+    if dev_err is not None:
+        _need(dev_err, "dev_err", torch.int32)
+    _on_device(q1=q1, q2=q2, k_cache=k_cache, k2_cache=k2_cache, v_cache=v_cache, page_table=page_table,
+               ctx_len=ctx_len, lam=lam, gamma=gamma if norm else None, out=out, dev_err=dev_err)
     a = DecodeArgs()
     a.dtype = _dtype_code(q1)
     a.B, a.H, a.H_kv, a.d_qk, a.d_v = B, H, Hkv, dqk, dv
@@ -366,14 +436,9 @@ def _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm
         raise ValueError("q1/q2 need unit innermost stride")
     a.sq1 = _c_int64_2(q1.stride(0), q1.stride(1))
     a.sq2 = _c_int64_2(q2.stride(0), q2.stride(1))
-    if not (k_cache.is_contiguous() and v_cache.is_contiguous()
-            and (k2_cache is None or k2_cache.is_contiguous())):
-        raise ValueError("caches must be contiguous")
     a.k1_cache = _ptr(k_cache)
     a.k2_cache = _ptr(k2_cache if k2_cache is not None else k_cache)
     a.v_cache = _ptr(v_cache)
-    if not (page_table.is_contiguous() and ctx_len.is_contiguous()):
-        raise ValueError("page_table and ctx_len must be contiguous int32 tensors")
     a.page_table = _ptr(page_table)
     a.ctx_len = _ptr(ctx_len)
     a.lambda_ = _ptr(lam)

@@ -116,10 +116,9 @@ int diffattn_backward(const diffattn_backward_args *a, void *workspace, size_t w
 int diffattn_lambda_backward(const float *lq1, const float *lk1, const float *lq2, const float *lk2, int H,
                              int d_lambda, const float *dlambda, float *dlq1, float *dlk1, float *dlq2,
                              float *dlk2, void *stream) {
-    if (!lq1 || !lk1 || !lq2 || !lk2 || !dlambda || !dlq1 || !dlk1 || !dlq2 || !dlk2)
-        return set_error(DIFFATTN_EINVAL, "diffattn_lambda_backward: null pointer");
-    if (H < 1 || d_lambda < 1 || d_lambda > 4096)
-        return set_error(DIFFATTN_EINVAL, "diffattn_lambda_backward: need H >= 1 and 1 <= d_lambda <= 4096");
+    std::string msg;
+    int rc = da::check_lambda_backward(lq1, lk1, lq2, lk2, H, d_lambda, dlambda, dlq1, dlk1, dlq2, dlk2, &msg);
+    if (rc != DIFFATTN_OK) return set_error(rc, msg);
     hipError_t e = da::launch_lambda_backward(lq1, lk1, lq2, lk2, H, d_lambda, dlambda, dlq1, dlk1, dlq2, dlk2,
                                               (hipStream_t)stream);
     return hip_status(e, "diffattn_lambda_backward");

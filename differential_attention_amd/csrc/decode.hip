@@ -324,7 +324,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const int row = 8 * i + (lane >> 3);
-                        const uint32_t keep = (row < vis && row >= vlo) ? 0xffffffffu : 0u;
+                        // a bad page id was replaced by page 0: none of its values may enter
+                        const uint32_t keep = (S.ok && row < vis && row >= vlo) ? 0xffffffffu : 0u;
                         const uint2 a = e4m3x4_to_bf16(S.v[i].x), b2 = e4m3x4_to_bf16(S.v[i].y);
                         const uint2 c2 = e4m3x4_to_bf16(S.v[i].z), d2 = e4m3x4_to_bf16(S.v[i].w);
                         // features 16 (lane % 8) .. +15 are 16-byte chunks 2 (lane % 8) and
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int row = 4 * i + grp;
-                        const uint32_t keep = (row < vis && row >= vlo) ? 0xffffffffu : 0u;  // select by value
+                        const uint32_t keep = (S.ok && row < vis && row >= vlo) ? 0xffffffffu : 0u;  // select by value
                         uint4 v = S.v[i];
                         v.x &= keep;
                         v.y &= keep;

@@ -86,6 +86,40 @@ int check_lambda(const float *lq1, const float *lk1, const float *lq2, const flo
     return DIFFATTN_OK;
 }
 
+int check_lambda_backward(const float *lq1, const float *lk1, const float *lq2, const float *lk2, int H,
+                          int d_lambda, const float *dlambda, const float *dlq1, const float *dlk1,
+                          const float *dlq2, const float *dlk2, std::string *msg) {
+    if (H < 1) return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda_backward: H must be >= 1");
+    if (d_lambda < 1 || d_lambda > 4096)
+        return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda_backward: d_lambda must be in [1, 4096]");
+    const float *ins[5] = {lq1, lk1, lq2, lk2, dlambda};
+    const float *outs[4] = {dlq1, dlk1, dlq2, dlk2};
+    for (const float *p : ins)
+        if (!p) return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda_backward: null pointer");
+    for (const float *p : outs)
+        if (!p) return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda_backward: null pointer");
+    for (const float *p : ins)
+        if (!aligned(p, 4)) return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda_backward: misaligned input");
+    for (const float *p : outs)
+        if (!aligned(p, 4)) return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda_backward: misaligned output");
+    const uintptr_t vec = (uintptr_t)H * (uintptr_t)d_lambda * 4;
+    Extent ei[5], eo[4];
+    for (int i = 0; i < 5; ++i)
+        ei[i] = Extent{(uintptr_t)ins[i], (uintptr_t)ins[i] + (i < 4 ? vec : (uintptr_t)H * 4)};
+    for (int i = 0; i < 4; ++i) eo[i] = Extent{(uintptr_t)outs[i], (uintptr_t)outs[i] + vec};
+    // the kernel reads every input while it writes the outputs: no output may
+    // share memory with an input or with another output
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(eo[i], ei[j]))
+                return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda_backward: an output overlaps an input");
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(eo[i], eo[j]))
+                return fail(msg, DIFFATTN_EINVAL, "diffattn_lambda_backward: outputs overlap");
+    }
+    return DIFFATTN_OK;
+}
+
 int check_prefill(const diffattn_prefill_args *a, PrefillPlan *plan, std::string *msg) {
     *plan = PrefillPlan();
     if (!a) return fail(msg, DIFFATTN_EINVAL, "diffattn_prefill: null argument struct");

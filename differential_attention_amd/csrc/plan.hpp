@@ -79,4 +79,10 @@ int check_decode(const diffattn_decode_args *a, DecodePlan *plan, std::string *m
 int check_lambda(const float *lq1, const float *lk1, const float *lq2, const float *lk2, int H,
                  int d_lambda, int depth, const float *out, std::string *msg);
 
+// Validate diffattn_lambda_backward arguments: sizes, null pointers, 4-byte
+// alignment, and no output overlapping an input or another output.
+int check_lambda_backward(const float *lq1, const float *lk1, const float *lq2, const float *lk2, int H,
+                          int d_lambda, const float *dlambda, const float *dlq1, const float *dlk1,
+                          const float *dlq2, const float *dlk2, std::string *msg);
+
 }  // namespace da

@@ -312,3 +312,31 @@ def test_backward_rejects_small_workspace(lib):
 def test_prefill_rejects_partial_statistics(lib):
     a = _prefill_args(o1=FAKE + 6 * (1 << 24))
     assert _rc(lib, a) == da.EINVAL
+
+
+def test_lambda_backward_rejects(lib):
+    f = lib.diffattn_lambda_backward
+    H, dl = 4, 8
+    vec = H * dl * 4
+    ins = [FAKE + i * 4096 for i in range(4)]       # lq1, lk1, lq2, lk2
+    dlam = FAKE + 4 * 4096
+    outs = [FAKE + (8 + i) * 4096 for i in range(4)]  # dlq1, dlk1, dlq2, dlk2
+
+    def rc(ins_, dlam_, outs_, H_=H, dl_=dl):
+        return f(*ins_, H_, dl_, dlam_, *outs_, None)
+
+    assert rc(ins, dlam, outs, H_=0) == da.EINVAL
+    assert rc(ins, dlam, outs, dl_=0) == da.EINVAL
+    assert rc(ins, dlam, outs, dl_=4097) == da.EINVAL
+    assert rc(ins, None, outs) == da.EINVAL
+    assert rc(ins, dlam, outs[:3] + [None]) == da.EINVAL
+    assert rc(ins, dlam, [outs[0] + 2] + outs[1:]) == da.EINVAL            # misaligned output
+    assert "misaligned" in lib.diffattn_last_error().decode()
+    assert rc([ins[0] + 1] + ins[1:], dlam, outs) == da.EINVAL             # misaligned input
+    assert rc(ins, dlam, [ins[0]] + outs[1:]) == da.EINVAL                 # in place: dlq1 == lq1
+    assert "overlaps an input" in lib.diffattn_last_error().decode()
+    assert rc(ins, dlam, outs[:3] + [ins[3] + vec - 4]) == da.EINVAL       # partial overlap with lk2
+    assert rc(ins, dlam, outs[:3] + [dlam]) == da.EINVAL                  # overlaps dlambda
+    assert rc(ins, dlam, [outs[0], outs[0] + vec - 4] + outs[2:]) == da.EINVAL  # outputs overlap
+    assert "outputs overlap" in lib.diffattn_last_error().decode()
+    assert lib.diffattn_last_error().decode().startswith("diffattn_lambda_backward")
