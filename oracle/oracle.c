@@ -40,7 +40,9 @@
  *     page_table[b][t / page], slot t % page.
  *
  * Inputs are fp32 arrays (bf16 inputs are widened exactly by the caller);
- * all arithmetic is fp64 and every sum runs in index order.
+ * all arithmetic is fp64 and every sum runs in index order (built without
+ * contraction into fused multiply-adds and without reassociation, so the
+ * compiler's vectorisation across independent sums changes no result).
  */
 #include <math.h>
 #include <stdint.h>
@@ -97,6 +99,26 @@ static double dot(const float *a, const float *b, int d)
     return acc;
 }
 
+/* q . b[0], ..., q . b[3]: four dot products formed side by side, each
+ * summed in index order exactly as dot() sums it (the four sums are
+ * independent, so evaluating them together changes no result, only the
+ * speed). */
+static void dot4(const float *q, const float *const *b, int d, double out[4])
+{
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    for (int k = 0; k < d; ++k) {
+        const double x = (double)q[k];
+        s0 += x * (double)b[0][k];
+        s1 += x * (double)b[1][k];
+        s2 += x * (double)b[2][k];
+        s3 += x * (double)b[3][k];
+    }
+    out[0] = s0;
+    out[1] = s1;
+    out[2] = s2;
+    out[3] = s3;
+}
+
 /* One output row. kp1/kp2/vp hold the n visible keys/values in key order.
  * Scratch s1, s2 hold n doubles each. Writes y[0..d_v). */
 static void diff_row(const float *q1, const float *q2,
@@ -110,8 +132,18 @@ static void diff_row(const float *q1, const float *q2,
         for (int c = 0; c < d_v; ++c) y[c] = 0.0;
         return;
     }
-    /* [L] scores of both branches */
-    for (int64_t j = 0; j < n; ++j) {
+    /* [L] scores of both branches (four keys at a time, then the rest) */
+    int64_t j0 = 0;
+    for (; j0 + 4 <= n; j0 += 4) {
+        double d1[4], d2[4];
+        dot4(q1, kp1 + j0, d_qk, d1);
+        dot4(q2, kp2 + j0, d_qk, d2);
+        for (int t = 0; t < 4; ++t) {
+            s1[j0 + t] = d1[t] * scale;
+            s2[j0 + t] = d2[t] * scale;
+        }
+    }
+    for (int64_t j = j0; j < n; ++j) {
         s1[j] = dot(q1, kp1[j], d_qk) * scale;
         s2[j] = dot(q2, kp2[j], d_qk) * scale;
     }

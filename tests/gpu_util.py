@@ -40,9 +40,10 @@ def check(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     d = np.abs(got - ref)
     mx = float(d.max()) if d.size else 0.0
+    where = np.unravel_index(int(d.argmax()), d.shape) if d.size else ()
     if dtype == "bf16":
         fro = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
-        say(f"  {what}: max|d| {mx:.3e} rel-fro {fro:.3e} over {d.size} elements")
+        say(f"  {what}: max|d| {mx:.3e} at {tuple(int(x) for x in where)} rel-fro {fro:.3e} over {d.size} elements")
         assert mx <= BF16_MAX_ABS, f"{what}: max abs error {mx}"
         assert fro <= BF16_REL_FRO, f"{what}: relative Frobenius error {fro}"
     else:
