@@ -40,8 +40,16 @@
 //    uses, two at a time (v_dot2_f32_bf16 against ones).
 //  * LDS tiles have no padding; 16-byte chunks are XOR-swizzled per row so the
 //    K-operand reads and the transposing V reads are free of bank conflicts.
-//  * Lazy rescale: a wave's reference max moves only when a block max exceeds
-//    it by 2^8, so the accumulators are rarely rescaled.
+//  * Fixed-reference sweep: when every row sees at least 256 keys and the
+//    scores of 32 sampled keys span at most 12 log2 units in every row, the
+//    queries are pre-scaled by scale * log2(e) (rounded once to bf16) and the
+//    probabilities are 2^s against a fixed reference of 0: no running max,
+//    no subtraction, no rescale (about half the softmax's VALU work). The
+//    sums are checked once, after the sweep; a row out of range sends the
+//    work-group through the exact sweep from the start.
+//  * Exact sweep (otherwise, and with stored statistics): lazy rescale, a
+//    wave's reference max moves only when a block max exceeds it by 2^8, so
+//    the accumulators are rarely rescaled.
 //  * Causal: key tiles past the work-group's last row are never loaded; a wave
 //    stops at its diagonal sub-block, the only one it masks (with the ragged
 //    end of the sequence). Work-groups with the longest rows run first.
@@ -56,6 +64,7 @@
 #include "tiles.hpp"
 
 #include <climits>
+#include <type_traits>
 
 namespace da {
 
@@ -63,6 +72,18 @@ namespace {
 
 constexpr int kWM = 32;               // query rows per wave
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
+// Fixed-reference sweep: with the queries pre-scaled by scale * log2(e) the
+// products give the scores in log2 units, and the probabilities are taken as
+// 2^s against a fixed reference of 0 (no running max, no subtraction, no
+// rescale). That is the same softmax as long as the sums stay in range, which
+// is checked once, after the sweep: a row whose sum is not within
+// [kFastMinSum, kFastMaxSum] (a score above about 64 or a row whose scores are
+// all below about -60, in log2 units) or whose accumulators are not finite
+// sends its work-group through the exact sweep (running max, lazy rescale).
+constexpr float kFastMinSum = 8.673617379884035e-19f;  // 2^-60
+constexpr int kFastMinKeys = 256;     // rows with fewer visible keys take the exact sweep
+constexpr float kFastMaxRange = 12.0f;  // largest sampled score span (log2 units) of the fixed-reference sweep
+constexpr float kFastMaxSum = 1.8446744073709552e19f;  // 2^64
 
 // branch-split decomposition for a head dimension (see the header comment)
 template <int DQK>
@@ -82,6 +103,7 @@ struct Bf16Params {
     float *o1, *o2, *lse1, *lse2;  // optional statistics for the backward pass (all or none)
     int B, H, H_kv, group, N, causal, window, row_blocks, xcd_units;
     int group_norm;  // the norm subtracts the channel mean first (GroupNorm per head)
+    int prescale;    // the fixed-reference sweep is allowed (off when statistics are stored)
     float sc_log2;  // scale * log2(e)
     float eps, one_minus_init;
 };
@@ -101,10 +123,12 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     constexpr int kStageBytes = (S::kOn && T::kStage < 32768) ? 32768 : T::kStage;
     __shared__ __attribute__((aligned(1024))) unsigned char st0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[kStageBytes];
+    __shared__ int redo_flag;  // a row left the fixed-reference range: redo the sweep exactly
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
+    if (tid == 0) redo_flag = 0;  // read only after the sweep's barriers
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int br0 = S::kOn ? (wave & 1) : 0;   // first branch of this wave (0: Q1/K1, 1: Q2/K2)
@@ -139,9 +163,14 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     const int wrow0 = q0 + rg * kWM;  // first query row of this wave
     const int myrow = wrow0 + l32;    // the query row of this lane
 
+    const __bf16 *kb1 = p.k1 + b * p.sk1[0] + g * p.sk1[1];
+    const __bf16 *kb2 = p.k2 + b * p.sk2[0] + g * p.sk2[1];
+    const __bf16 *vb = p.v + b * p.sv[0] + g * p.sv[1];
+    const int64_t sk1n = p.sk1[2], sk2n = p.sk2[2], svn = p.sv[2];
+
     // ---- Q fragments of this wave's branches (B operands): Q[myrow][16 kc + 8 hh .. +7]
     bf16x8 qf[NBR][KC];
-    {
+    auto load_q = [&]() DA_INLINE {
         const int row = min(myrow, p.N - 1);  // rows past the end compute garbage, never stored
 #pragma unroll
         for (int j = 0; j < NBR; ++j) {
@@ -150,12 +179,72 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) qf[j][kc] = as_bf16x8(ldg16(q + 8 * hh + 16 * kc));
         }
-    }
+    };
+    load_q();
 
-    const __bf16 *kb1 = p.k1 + b * p.sk1[0] + g * p.sk1[1];
-    const __bf16 *kb2 = p.k2 + b * p.sk2[0] + g * p.sk2[1];
-    const __bf16 *vb = p.v + b * p.sv[0] + g * p.sv[1];
-    const int64_t sk1n = p.sk1[2], sk2n = p.sk2[2], svn = p.sv[2];
+    // ---- exact or fixed-reference sweep (see kFastMinSum) for this work-group.
+    // The fixed-reference sweep needs the queries pre-scaled: q * scale *
+    // log2(e), rounded once to bf16, so that the products give the scores in
+    // log2 units. That rounding moves each score by about 2^-10 of the spread
+    // of its terms across keys, so the sweep is taken only where that stays
+    // small against the rounding of the probabilities themselves:
+    //  * every row sees at least kFastMinKeys keys (in rows of a few keys
+    //    whose two branches nearly cancel, the V1 norm magnifies any error);
+    //  * the scores of 32 keys every row sees (sampled before the sweep) span
+    //    at most kFastMaxRange in every row.
+    // Neither holds with stored statistics (the backward recomputes the exact
+    // scores) and neither is needed for the result to be right: the exact
+    // sweep is always available.
+    const int min_keys = WIN ? min(p.causal ? q0 + 1 : p.N, p.window) : (p.causal ? q0 + 1 : p.N);
+    // first sampled key: the window start of the work-group's last row, so
+    // that keys ks .. ks+31 are visible to every row (a window that cuts no
+    // row's keys samples the same keys as no window)
+    const int ks = WIN ? max(0, min(q0 + S::kBM, p.N) - p.window) : 0;
+    bool fast = p.prescale && min_keys >= kFastMinKeys && ks + 31 <= (p.causal ? q0 : p.N - 1);
+    float scl = p.sc_log2;  // multiplier from the products' scores to log2 units
+    if (fast) {  // work-group-uniform
+#pragma unroll
+        for (int j = 0; j < NBR; ++j)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const bf16x8 x = qf[j][kc];
+                qf[j][kc] = pack8((float)x[0] * p.sc_log2, (float)x[1] * p.sc_log2, (float)x[2] * p.sc_log2,
+                                  (float)x[3] * p.sc_log2, (float)x[4] * p.sc_log2, (float)x[5] * p.sc_log2,
+                                  (float)x[6] * p.sc_log2, (float)x[7] * p.sc_log2);
+            }
+        // the sample: keys ks .. ks+31 against this lane's row, straight from
+        // global memory (S^T = K Q^T as in the sweep, unpermuted key order)
+        float span = 0.0f;
+        {
+            const int key = ks + l32;
+#pragma unroll
+            for (int j = 0; j < NBR; ++j) {
+                const __bf16 *kr = ((br0 + j) ? kb2 + (int64_t)key * sk2n : kb1 + (int64_t)key * sk1n) + 8 * hh;
+                f32x16 sv = f32x16{};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) sv = mfma32(as_bf16x8(ldg16(kr + 16 * kc)), qf[j][kc], sv);
+                float mx = sv[0], mn = sv[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) {
+                    mx = fmaxf(mx, sv[r]);
+                    mn = fminf(mn, sv[r]);
+                }
+                span = fmaxf(span, halves_max(mx) + halves_max(-mn));
+            }
+        }
+        const bool wide = !(span <= kFastMaxRange) && myrow < p.N;
+        __syncthreads();  // redo_flag cleared
+        if (__any(wide) && lane == 0) redo_flag = 1;
+        __syncthreads();
+        if (redo_flag) {
+            fast = false;
+            load_q();  // back to the exact queries
+        } else {
+            scl = 1.0f;
+        }
+        __syncthreads();  // every wave has read the flag
+        if (tid == 0) redo_flag = 0;  // for the check after the sweep (read after its barriers)
+    }
 
     const int kend = p.causal ? min(p.N, q0 + S::kBM) : p.N;
     const int ntiles = (kend + kBN - 1) / kBN;
@@ -253,7 +342,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 #pragma unroll
         for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
         mx = fmaxf(mx, s[15]);
-        const float mxs = halves_max(mx) * p.sc_log2;
+        const float mxs = halves_max(mx) * scl;
         if (__any(mxs > mr + kRescaleLog2)) {
             const float mnew = fmaxf(mr, mxs);
             const float alpha = (mr == mnew) ? 1.0f : exp2_fast(mr - mnew);
@@ -264,7 +353,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         }
         const float msub = (mr == -INFINITY) ? 0.0f : mr;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = exp2_fast(fmaf(s[r], p.sc_log2, -msub));
+        for (int r = 0; r < 16; ++r) s[r] = exp2_fast(fmaf(s[r], scl, -msub));
         bf16x2 pp[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) pp[i] = pack2(s[2 * i], s[2 * i + 1]);
@@ -281,7 +370,36 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         pb1 = bf16x8{pp[4][0], pp[4][1], pp[5][0], pp[5][1], pp[6][0], pp[6][1], pp[7][0], pp[7][1]};
     };
 
-    auto step = [&](const unsigned char *base, int sb, bool mask, int lim, int lo) DA_INLINE {
+    // the fixed-reference form of one branch: p = 2^s (scores already in log2
+    // units), bf16 probabilities and this block's row sum lb of the rounded values
+    auto softmax_fast = [&](f32x16 s, bool mask, int lim, int lo, bf16x8 &pb0, bf16x8 &pb1,
+                            float &lb) DA_INLINE {
+        if (mask) {
+            asm volatile("");
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (key_of_reg(r) >= lim || key_of_reg(r) < lo) s[r] = -INFINITY;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = exp2_fast(s[r]);
+        bf16x2 pp[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pp[i] = pack2(s[2 * i], s[2 * i + 1]);
+        float l0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], ones, 0.0f, false);
+        float l1 = __builtin_amdgcn_fdot2_f32_bf16(pp[4], ones, 0.0f, false);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+            l0 = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, l0, false);
+            l1 = __builtin_amdgcn_fdot2_f32_bf16(pp[4 + i], ones, l1, false);
+        }
+        lb = l0 + l1;
+        pb0 = bf16x8{pp[0][0], pp[0][1], pp[1][0], pp[1][1], pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
+        pb1 = bf16x8{pp[4][0], pp[4][1], pp[5][0], pp[5][1], pp[6][0], pp[6][1], pp[7][0], pp[7][1]};
+    };
+    // one 32-key sub-block: scores, softmax (fixed-reference or exact form,
+    // chosen at compile time by the tag), value products
+    auto step = [&](auto fast_tag, const unsigned char *base, int sb, bool mask, int lim, int lo) DA_INLINE {
+        constexpr bool kFast = decltype(fast_tag)::value;
         const unsigned char *vt = base + T::kNK * T::kKBytes;
         // every branch's score products first: with two branches per wave the
         // two product chains interleave, and the rescale test of one branch
@@ -290,8 +408,18 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 #pragma unroll
         for (int j = 0; j < NBR; ++j) sc[j] = qk_branch(base + (SHARED_K ? 0 : (br0 + j) * T::kKBytes), qf[j], sb);
         bf16x8 pb[NBR][2];
+        if constexpr (kFast) {
 #pragma unroll
-        for (int j = 0; j < NBR; ++j) softmax_branch(sc[j], mask, lim, lo, m[j], l[j], o[j], pb[j][0], pb[j][1]);
+            for (int j = 0; j < NBR; ++j) {
+                float lb;
+                softmax_fast(sc[j], mask, lim, lo, pb[j][0], pb[j][1], lb);
+                l[j] += lb;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NBR; ++j)
+                softmax_branch(sc[j], mask, lim, lo, m[j], l[j], o[j], pb[j][0], pb[j][1]);
+        }
         // O^T += V^T P^T, one V read for every branch of the wave; the next
         // step's V operand is read while this step's products run
         // step i covers (k step t, dv block dc). With one branch per wave the k
@@ -318,20 +446,20 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     };
 
     // ---- the key sweep: even tiles in stage 0, odd tiles in stage 1
-    auto tile_body = [&](const unsigned char *base, int t) DA_INLINE {
+    auto tile_body = [&](auto ft, const unsigned char *base, int t) DA_INLINE {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int j = 2 * t + sb;
             if (j < jlo || j >= nsub) continue;  // wholly outside every row's window / past the diagonal
             if (j < nsub - 1 && j >= jmask) {
-                step(base, sb, false, 0, 0);
+                step(ft, base, sb, false, 0, 0);
             } else {
                 // diagonal / ragged-end sub-block (keys >= lim masked) and
                 // window-start sub-blocks (keys < lo masked), relative to key0
                 const int key0 = j * 32 + 8 * hh;
                 const int lim = (p.causal ? min(myrow + 1, p.N) : p.N) - key0;
                 const int lo = WIN ? myrow - win + 1 - key0 : INT_MIN / 2;
-                step(base, sb, true, lim, lo);
+                step(ft, base, sb, true, lim, lo);
             }
         }
     };
@@ -344,38 +472,77 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     // compiler merge the two variants of a step and evaluate the mask for
     // every sub-block. Phase boundaries sit at even tile offsets from tlo, so
     // each phase starts in stage 0 with its first tile already issued.
-    auto tile_body_open = [&](const unsigned char *base, int t) DA_INLINE {
+    auto tile_body_open = [&](auto ft, const unsigned char *base, int t) DA_INLINE {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
-            if (2 * t + sb < nsub - 1) step(base, sb, false, 0, 0);
+            if (2 * t + sb < nsub - 1) step(ft, base, sb, false, 0, 0);
     };
-    auto phase = [&](auto body, int t0, int t1) DA_INLINE {
+    auto phase = [&](auto ft, auto body, int t0, int t1) DA_INLINE {
         for (int t = t0; t < t1; t += 2) {
             wait_vmem_all();
             __syncthreads();  // tile t visible to all waves; tile t-1 no longer read
             if (t + 1 < ntiles) issue_tile(t + 1, st1);
-            body(st0, t);
+            body(ft, st0, t);
             if (t + 1 >= t1) break;  // only the last phase can end on an odd offset
             wait_vmem_all();
             __syncthreads();  // tile t+1 visible to all waves; tile t no longer read
             if (t + 2 < ntiles) issue_tile(t + 2, st0);
-            body(st1, t + 1);
+            body(ft, st1, t + 1);
         }
     };
-    if (tlo < ntiles) issue_tile(tlo, st0);
-    if constexpr (S::kOn) {
-        constexpr int kTail = S::kBM / kBN;  // tiles holding the waves' diagonal sub-blocks
-        const int ta = WIN ? min(ntiles, tlo + 4) : tlo;
-        const int tb = max(ta, tlo + 2 * ((ntiles - kTail - tlo) / 2));
-        if (WIN) phase(tile_body, tlo, ta);
-        phase(tile_body_open, ta, tb);
-        phase(tile_body, tb, ntiles);
-    } else {
-        // the two-branch kernels run one phase: the second copy of the step
-        // that separate phases need costs them more (register spills) than the
-        // guarded mask branch it saves
-        phase(tile_body, tlo, ntiles);
+    auto sweep = [&](auto ft) DA_INLINE {
+        if (tlo < ntiles) issue_tile(tlo, st0);
+        if constexpr (S::kOn) {
+            constexpr int kTail = S::kBM / kBN;  // tiles holding the waves' diagonal sub-blocks
+            const int ta = WIN ? min(ntiles, tlo + 4) : tlo;
+            const int tb = max(ta, tlo + 2 * ((ntiles - kTail - tlo) / 2));
+            if (WIN) phase(ft, tile_body, tlo, ta);
+            phase(ft, tile_body_open, ta, tb);
+            phase(ft, tile_body, tb, ntiles);
+        } else {
+            // the two-branch kernels run one phase: the second copy of the step
+            // that separate phases need costs them more (register spills) than the
+            // guarded mask branch it saves
+            phase(ft, tile_body, tlo, ntiles);
+        }
+    };
+    // The fixed-reference sweep first (when the queries are pre-scaled), then,
+    // if any row of the work-group left its range, the exact sweep from the
+    // start. The decision is the work-group's (one flag in LDS), so every wave
+    // runs the same barriers.
+    bool exact = true;
+    if (fast) {
+        sweep(std::true_type{});
+        bool bad = false;
+#pragma unroll
+        for (int j = 0; j < NBR; ++j) {
+            const float ls = halves_sum(l[j]);
+            bad = bad || !(ls >= kFastMinSum && ls <= kFastMaxSum);
+#pragma unroll
+            for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) bad = bad || !__builtin_isfinite(o[j][dc][r]);
+        }
+        bad = bad && myrow < p.N;
+        if (__any(bad) && lane == 0) redo_flag = 1;
+        __syncthreads();  // every wave has left the sweep and set its flag
+        exact = redo_flag != 0;
+        if (exact) {
+#pragma unroll
+            for (int j = 0; j < NBR; ++j) {
+#pragma unroll
+                for (int dc = 0; dc < 4; ++dc) o[j][dc] = f32x16{};
+                m[j] = -INFINITY;
+                l[j] = 0.0f;
+            }
+            load_q();  // the exact sweep takes the exact queries
+            scl = p.sc_log2;
+        } else {
+#pragma unroll
+            for (int j = 0; j < NBR; ++j) m[j] = 0.0f;  // the reference the sums were taken against
+        }
     }
+    if (exact) sweep(std::false_type{});
 
     // ---- epilogue: y = O1 / l1 - lambda O2 / l2 (then the V1 norm), bf16 store
 #pragma unroll
@@ -535,6 +702,7 @@ hipError_t launch_prefill_bf16(const diffattn_prefill_args &a, float scale, floa
     const int kv_units = a.B * a.H_kv;
     p.xcd_units = (kv_units % 8 == 0) ? kv_units / 8 : 0;
     p.sc_log2 = scale * kLog2e;
+    p.prescale = a.o1 == nullptr;  // the statistics for the backward keep the exact scores
     p.eps = a.eps;
     p.one_minus_init = 1.0f - lambda_init;
     const int64_t blocks = (int64_t)a.B * a.H * p.row_blocks;

@@ -268,3 +268,47 @@ def test_longctx_v1_all_rows(torch, da):
     say("longctx_v1 full: all 524288 rows against the oracle")
     out = c.run().float().cpu().numpy()
     check_all_rows_by_head(c, out, "longctx_v1 all rows")
+
+
+# ---------------------------------------------------------------- score range: exact sweep after the fast one
+# The bf16 kernels first sweep with probabilities 2^s against a fixed
+# reference (no running max); a work-group whose rows leave the range where
+# that is exact sweeps again with the running max. These inputs put scores
+# far above (2^s would overflow to inf) or far below (2^s would underflow to
+# 0) that range, so a missing or wrong second sweep gives non-finite rows.
+
+@pytest.mark.parametrize("form", ["v1", "v2"])
+@pytest.mark.parametrize("scale", [2.0, 16.0])
+def test_bf16_large_scores(torch, da, form, scale):
+    p = _bf16_case(form, 333, True, B=1, seed=41)
+    c = PrefillCase(p)
+    say(f"bf16 {form} N 333 scale {scale} (scores up to ~{scale * 9:.0f} nats)")
+    got = c.run(scale=scale).float().cpu().numpy()
+    k1 = p.f32("k1")
+    ref = oracle.prefill(p.f32("q1"), p.f32("q2"), k1, k1 if p.shared_k else p.f32("k2"), p.f32("v"), c.lam64,
+                         depth=p.depth, causal=True, norm=p.norm, gamma=p.gamma, eps=p.eps, scale=scale)
+    check(got, ref, "bf16", f"{form} scale {scale}")
+
+
+@pytest.mark.parametrize("form", ["v1", "v2"])
+def test_bf16_all_scores_far_below_zero(torch, da, form):
+    # every key carries +10 u and every query -10 u (u a unit vector), so all
+    # scores sit near -100 * scale nats; the softmax depends only on the rest
+    p = _bf16_case(form, 300, True, B=1, seed=43)
+    u = np.zeros(p.d_qk, np.float32)
+    u[3] = 1.0
+    shift = lambda x, s: W.f32_to_bf16(W.bf16_to_f32(x) + s * u)
+    if p.q_full is not None:
+        p.q_full = shift(p.q_full, -10.0)
+        p.q1, p.q2 = p.q_full[:, 0::2], p.q_full[:, 1::2]
+    else:
+        p.q1, p.q2 = shift(p.q1, -10.0), shift(p.q2, -10.0)
+    p.k1 = shift(p.k1, 10.0)
+    p.k2 = p.k1 if p.shared_k else shift(p.k2, 10.0)
+    c = PrefillCase(p)
+    say(f"bf16 {form} N 300, scores near -100 * scale")
+    got = c.run(scale=2.0).float().cpu().numpy()
+    k1 = p.f32("k1")
+    ref = oracle.prefill(p.f32("q1"), p.f32("q2"), k1, k1 if p.shared_k else p.f32("k2"), p.f32("v"), c.lam64,
+                         depth=p.depth, causal=True, norm=p.norm, gamma=p.gamma, eps=p.eps, scale=2.0)
+    check(got, ref, "bf16", f"{form} negative scores")
