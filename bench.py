@@ -3,23 +3,29 @@
 
 One step is one pass of the whole path over one batch of synthetic input:
   lambda   diffattn_lambda for the prefill heads
-  prefill  diffattn_prefill on prefill_v1: V1 form, B 2, H 16, N 4096,
-           d_qk 64, d_v 128, causal, bf16, RMSNorm epilogue
+  prefill  diffattn_prefill on longctx_v1: V1 form, B 1, H 8, N 65536,
+           d_qk 64, d_v 128, causal, bf16, RMSNorm epilogue, planted keys
+           (the largest single-GPU prefill workload)
   lambda   diffattn_lambda for the decode heads
   decode   diffattn_decode on decode_v2: V2 form, 64 sequences, context
            U{8192..32768}, 8 KV heads, 64 query heads, d 128, page 64, bf16
 Inputs are resident in HBM before the timed region. Each call is bracketed by
-HIP events on the stream the library launches on, so per-kernel averages come
-from the same timed steps.
+HIP events on the stream the library launches on (the prefill runs for
+milliseconds, so the host stays ahead of the device and the events time the
+kernels, not the launches). The two other prefill workloads, prefill_v2
+(V2 GQA, N 16384) and prefill_v1 (V1, B 2, H 16, N 4096), are timed after the
+steps, each as a batch of back-to-back calls between two events.
 
-Output: one JSON line. ``value`` is prefill throughput, FLOPs counted as
-B*H*(N^2/2)*2*(2*d_qk + 2*d_v) (both branches, QK and PV, causal pairs
-halved), over the mean time of the lambda + prefill part of a step; the
-``decode`` object gives the decode part's algorithmic HBM bytes (every
-visible token's K and V once, plus Q, output and page-table entries) per
-second. ``roofline`` is the prefill kernel against the bf16 dense MFMA peak,
-``decode.roofline`` the decode call against HBM bandwidth. ``cpu_baseline``
-times the fp64 CPU oracle on a bounded random sample of prefill rows.
+Output: one JSON line. ``value`` is the step's prefill throughput, FLOPs
+counted as B*H*(N^2/2)*2*(2*d_qk + 2*d_v) (both branches, QK and PV, causal
+pairs halved), over the mean time of the lambda + prefill part of a step; the
+``decode`` object gives the decode part's algorithmic HBM bytes (every visible
+token's K and V once, plus Q, output and page-table entries) per second;
+``prefill_other`` the other two prefill workloads. ``roofline`` is the
+step's prefill kernel against the bf16 dense MFMA peak, ``decode.roofline``
+the decode call against HBM bandwidth. ``cpu_baseline`` times the fp64 CPU
+oracle on a bounded random sample of the headline workload's rows, with one
+entry per workload under ``per_workload``.
 """
 from __future__ import annotations
 
@@ -64,12 +70,18 @@ def decode_bytes(d):
     """Algorithmic HBM bytes of one decode call: every visible token's keys
     (one cache, or one per branch) and values once, the queries, the output,
     the page-table entries used and ctx_len (plus gamma for the V1 norm)."""
-    L = d.ctx_len.astype(np.int64)
+    return decode_bytes_of(d, d.ctx_len)
+
+
+def decode_bytes_of(d, ctx_len):
+    """decode_bytes for the sequences whose lengths are ctx_len."""
+    L = np.asarray(ctx_len).astype(np.int64)
+    B = L.size
     nk = 1 if d.shared_k else 2
     kv = int(L.sum()) * d.H_kv * (nk * d.d_qk + d.d_v) * d.kv_bytes  # bf16: 2 bytes, fp8: 1
-    q = d.B * 2 * d.H * d.d_qk * 2
-    out = d.B * d.H * d.d_v * 2
-    table = int(((L + d.page - 1) // d.page).sum()) * 4 + d.B * 4
+    q = B * 2 * d.H * d.d_qk * 2
+    out = B * d.H * d.d_v * 2
+    table = int(((L + d.page - 1) // d.page).sum()) * 4 + B * 4
     gamma = d.H * d.d_v * 4 if d.norm else 0
     return kv + q + out + table + gamma
 
@@ -124,27 +136,66 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(p, lam64, budget_s):
-    """Oracle FLOP/s on a random sample of prefill rows (same inputs)."""
+def cpu_baseline_prefill(p, budget_s, seed=1234):
+    """Oracle FLOP/s on a random sample of prefill rows (same inputs): about
+    budget_s seconds of oracle time, FLOPs counted per visible key as for the
+    GPU (both branches, QK and PV)."""
     import oracle
-    rng = np.random.default_rng(1234)
-    q1, q2, k1, k2, v = (p.f32(n) for n in ("q1", "q2", "k1", "k2", "v"))
+    rng = np.random.default_rng(seed)
+    lam64 = oracle.lambda_(p.lam_q1, p.lam_k1, p.lam_q2, p.lam_k2, p.depth)
+    q1, q2, k1, v = (p.f32(n) for n in ("q1", "q2", "k1", "v"))
+    k2 = k1 if p.shared_k else p.f32("k2")
     per_key = 2 * (2 * p.d_qk + 2 * p.d_v)
+    total = p.B * p.H * p.N
 
     def run(nrows):
-        rows = rng.choice(p.B * p.H * p.N, size=nrows, replace=False).astype(np.int64)
-        flops = float(((rows % p.N) + 1).sum()) * per_key
+        rows = np.sort(rng.choice(total, size=nrows, replace=False)).astype(np.int64)
+        visible = ((rows % p.N) + 1) if p.causal else np.full(rows.size, p.N)
+        flops = float(visible.sum()) * per_key
         t0 = time.perf_counter()
-        oracle.prefill(q1, q2, k1, k2, v, lam64, depth=p.depth, causal=True, norm=True,
+        oracle.prefill(q1, q2, k1, k2, v, lam64, depth=p.depth, causal=p.causal, norm=p.norm,
                        gamma=p.gamma, eps=p.eps, rows=rows)
         return flops, time.perf_counter() - t0
 
-    f0, t0 = run(64)                      # calibration
-    n = int(min(p.B * p.H * p.N, max(64, 64 * budget_s / max(t0, 1e-3))))
+    f0, t0 = run(min(total, 64))  # calibration
+    n = int(min(total, max(64, 64 * budget_s / max(t0, 1e-3))))
     f, t = run(n)
     return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n} random query rows of prefill_v1 (of {p.B * p.H * p.N}), fp64, "
-                      f"{t:.1f} s on {cpu_model()}, FLOPs counted per visible key as for the GPU"}
+            "sample": f"{n} random query rows of {p.name} (of {total}), fp64, {t:.1f} s on {cpu_model()}, "
+                      f"FLOPs counted per visible key as for the GPU"}
+
+
+def cpu_baseline_decode(d, budget_s, seed=1234):
+    """Oracle GB/s (algorithmic bytes, as for the GPU) on a random sample of
+    the decode's sequences. The sampled sequences' pages are gathered into a
+    small pool (the page table renumbered to it) before the timed call, so no
+    more than their share of the cache is widened to fp32."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    lam64 = oracle.lambda_(d.lam_q1, d.lam_k1, d.lam_q2, d.lam_k2, d.depth)
+
+    def run(nseq):
+        bs = np.sort(rng.choice(d.B, size=nseq, replace=False))
+        table, ctx = d.page_table[bs], d.ctx_len[bs]
+        used = np.unique(table[table >= 0])
+        remap = np.full(d.num_pages, -1, np.int32)
+        remap[used] = np.arange(used.size, dtype=np.int32)
+        sub_table = np.where(table >= 0, remap[np.maximum(table, 0)], -1).astype(np.int32)
+        k1c = d.values("k1_cache", d.k1_cache[used])
+        k2c = k1c if d.shared_k else d.values("k2_cache", d.k2_cache[used])
+        vc = d.values("v_cache", d.v_cache[used])
+        q1, q2 = d.f32("q1")[bs], d.f32("q2")[bs]
+        t0 = time.perf_counter()
+        oracle.decode(q1, q2, k1c, k2c, vc, sub_table, ctx, lam64, depth=d.depth, norm=d.norm, gamma=d.gamma,
+                      eps=d.eps)
+        return float(decode_bytes_of(d, ctx)), time.perf_counter() - t0
+
+    b0, t0 = run(1)
+    n = int(min(d.B, max(1, budget_s / max(t0, 1e-3))))
+    b, t = run(n)
+    return {"value": b / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} random sequences of {d.name} (of {d.B}), fp64, {t:.1f} s on {cpu_model()}, "
+                      f"bytes counted as for the GPU"}
 
 
 def single_workload(args, torch, da, W, dev):
@@ -271,7 +322,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time for the headline cpu_baseline (a third of it for each other workload)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profiling aid: run only one part of the step")
@@ -309,16 +361,31 @@ def main():
         return
 
     t_gen = time.perf_counter()
-    p = W.prefill_v1()
+    p = W.longctx_v1()
     d = W.decode_v2() if args.only != "prefill" else None
+    others = [W.prefill_v2(), W.prefill_v1()] if args.only is None else []
     log(f"inputs generated in {time.perf_counter() - t_gen:.1f} s")
 
-    # prefill tensors
-    P = {n: to_dev(getattr(p, n)) for n in ("q1", "q2", "k1", "k2", "v")}
-    lamv_p = [torch.from_numpy(x).to(dev) for x in (p.lam_q1, p.lam_k1, p.lam_q2, p.lam_k2)]
-    gamma = torch.from_numpy(p.gamma).to(dev)
-    out_p = torch.empty((p.B, p.H, p.N, p.d_v), dtype=torch.bfloat16, device=dev)
-    lam_p = torch.empty(p.H, dtype=torch.float32, device=dev)
+    def prefill_inputs(w):
+        if w.q_full is not None:
+            qf = to_dev(w.q_full)
+            q1, q2 = qf[:, 0::2], qf[:, 1::2]
+        else:
+            q1, q2 = to_dev(w.q1), to_dev(w.q2)
+        k1 = to_dev(w.k1)
+        k2 = k1 if w.shared_k else to_dev(w.k2)
+        return dict(q1=q1, q2=q2, k1=k1, k2=k2, v=to_dev(w.v),
+                    lamv=[torch.from_numpy(x).to(dev) for x in (w.lam_q1, w.lam_k1, w.lam_q2, w.lam_k2)],
+                    gamma=torch.from_numpy(w.gamma).to(dev) if w.norm else None,
+                    out=torch.empty((w.B, w.H, w.N, w.d_v), dtype=torch.bfloat16, device=dev),
+                    lam=torch.empty(w.H, dtype=torch.float32, device=dev))
+
+    def describe(w):
+        form = "V2 GQA" if w.shared_k else "V1"
+        return (f"{w.name} ({form}, B {w.B}, H {w.H}, H_kv {w.H_kv}, N {w.N}, d_qk {w.d_qk}, d_v {w.d_v}, causal, "
+                f"{'RMS' if w.norm else 'no norm'})")
+
+    P = prefill_inputs(p)
     # decode tensors
     if d is not None:
         qd = to_dev(d.q_full)
@@ -334,13 +401,18 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
+    def prefill_call(w, T):
+        da.lambda_(*T["lamv"], w.depth, out=T["lam"])
+        return lambda: da.prefill(T["q1"], T["q2"], T["k1"], T["k2"], T["v"], T["lam"], depth=w.depth,
+                                  causal=w.causal, norm=w.norm, gamma=T["gamma"], eps=w.eps, out=T["out"])
+
     def step(ev):
         if args.only != "decode":
             ev[0].record(stream)
-            da.lambda_(*lamv_p, p.depth, out=lam_p)
+            da.lambda_(*P["lamv"], p.depth, out=P["lam"])
             ev[1].record(stream)
-            da.prefill(P["q1"], P["q2"], P["k1"], P["k2"], P["v"], lam_p, depth=p.depth, causal=True,
-                       norm=True, gamma=gamma, eps=p.eps, out=out_p)
+            da.prefill(P["q1"], P["q2"], P["k1"], P["k2"], P["v"], P["lam"], depth=p.depth, causal=True,
+                       norm=True, gamma=P["gamma"], eps=p.eps, out=P["out"])
             ev[2].record(stream)
         if d is not None:
             ev[3].record(stream)
@@ -376,7 +448,7 @@ def main():
         pre_kernel = mean_ms(1, 2)
         res["prefill_part_ms"] = pre_part
         res["prefill_kernel_ms"] = pre_kernel
-        log(f"prefill: step part {pre_part * 1e3:.1f} us, kernel {pre_kernel * 1e3:.1f} us, "
+        log(f"prefill ({p.name}): step part {pre_part * 1e3:.1f} us, kernel {pre_kernel * 1e3:.1f} us, "
             f"{F / pre_kernel / 1e9:.1f} TFLOP/s")
     if d is not None:
         dbytes = decode_bytes(d)
@@ -387,6 +459,38 @@ def main():
         log(f"decode: step part {dec_part * 1e3:.1f} us, call {dec_call * 1e3:.1f} us, "
             f"{dbytes / dec_call / 1e6:.1f} GB/s")
 
+    # the other prefill workloads: batches of back-to-back calls between two
+    # events (a short kernel timed call by call would include the launch)
+    other = {}
+    for w in others:
+        T = prefill_inputs(w)
+        call = prefill_call(w, T)
+        n_calls = max(10, min(100, int(args.steps * 4 * p.N / w.N)))
+        for _ in range(max(3, args.warmup // 4)):
+            call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n_calls):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n_calls
+        Fw = prefill_flops(w.B, w.H, w.N, w.d_qk, w.d_v)
+        ach = Fw / (ms * 1e-3) / 1e12
+        kern = f"prefill_bf16_kernel<{w.d_qk}, {'true' if w.shared_k else 'false'}, {'true' if w.norm else 'false'}, false>"
+        other[w.name] = {"value": ach, "unit": "TFLOP/s", "ms_per_call": ms, "calls": n_calls,
+                         "workload": describe(w),
+                         "roofline": {"bound": "mfma", "kernel": kern, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                                      "traffic": load_traffic(w.name)}}
+        log(f"{w.name}: {ms * 1e3:.1f} us per call, {ach:.1f} TFLOP/s ({100 * ach / BF16_PEAK_TFLOPS:.1f}% of peak)")
+        del T
+        torch.cuda.empty_cache()
+
+    workload = describe(p)
+    if d is not None:
+        workload += (" + decode_v2 (V2 paged, 64 seqs, ctx U{8192..32768}, 8 KV / 64 Q heads, d 128, page 64)")
     line = {
         "metric": "prefill TFLOP/s (% bf16 MFMA peak) + decode GB/s (% HBM peak), 1 MI355X",
         "value": None, "unit": "TFLOP/s",
@@ -394,10 +498,7 @@ def main():
         "ms_per_step": total_ms / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "prefill_v1 (V1, B 2, H 16, N 4096, d_qk 64, d_v 128, causal, RMS) + "
-                               "decode_v2 (V2 paged, 64 seqs, ctx U{8192..32768}, 8 KV / 64 Q heads, "
-                               "d 128, page 64)",
-                   "global_batch": p.B, "seq_len": p.N, "parallelism": "none (1 GPU)"},
+        "config": {"workload": workload, "global_batch": p.B, "seq_len": p.N, "parallelism": "none (1 GPU)"},
         "wall_s": wall,
     }
     if args.only != "decode":
@@ -405,7 +506,7 @@ def main():
         ach = F / (res["prefill_kernel_ms"] * 1e-3) / 1e12
         line["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<64, false, true, false>",
                             "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": ach / BF16_PEAK_TFLOPS, "traffic": load_traffic("prefill_v1")}
+                            "frac": ach / BF16_PEAK_TFLOPS, "traffic": load_traffic(p.name)}
     if d is not None:
         gbs = dbytes / (res["decode_part_ms"] * 1e-3) / 1e9
         ach = dbytes / (res["decode_call_ms"] * 1e-3) / 1e9
@@ -414,13 +515,17 @@ def main():
                           "roofline": {"bound": "hbm", "kernel": "decode_split_kernel + decode_combine_kernel",
                                        "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic("decode_v2")}}
+    if other:
+        line["prefill_other"] = other
     if not args.no_cpu and args.only != "decode":
-        import oracle
-        lam64 = oracle.lambda_(p.lam_q1, p.lam_k1, p.lam_q2, p.lam_k2, p.depth)
         log("timing the CPU oracle ...")
-        line["cpu_baseline"] = cpu_baseline(p, lam64, args.cpu_budget)
+        per = {p.name: cpu_baseline_prefill(p, args.cpu_budget)}
+        for w in others:
+            per[w.name] = cpu_baseline_prefill(w, args.cpu_budget / 3)
+        if d is not None:
+            per[d.name] = cpu_baseline_decode(d, args.cpu_budget / 3)
+        line["cpu_baseline"] = dict(per[p.name], per_workload=per)
     print(json.dumps(line), flush=True)
-
 
 if __name__ == "__main__":
     main()
