@@ -325,22 +325,11 @@ def prefill_stats(q1, v):
     return f(B, H, N, dv), f(B, H, N, dv), f(B, H, N), f(B, H, N)
 
 
-def backward(q1, q2, k1, k2, v, lam, stats, dout, *, depth: int, causal: bool = True, norm: bool = False,
-             gamma=None, eps: float = 1e-5, scale: float = 0.0, window: int = 0, workspace=None, stream=None):
-    """Gradients of prefill(q1, q2, k1, k2, v, lam, ...) given dout (bf16
-    [B, H, N, d_v]) and the statistics (o1, o2, lse1, lse2) a prefill call with
-    stats=... stored. Returns a dict of fp32 tensors dq1, dq2, dk1, dk2, dv,
-    dlambda and (norm) dgamma; with k1 is k2 (one key tensor) dk1 is the whole
-    key gradient and dk2 is the same tensor."""
+def _backward_args(q1, q2, k1, k2, v, lam, stats, dout, g, depth, causal, norm, gamma, eps, scale, window):
     import torch
     B, H, N, dqk = q1.shape
     Hkv, dv_ = k1.shape[1], v.shape[3]
     shared = k1.data_ptr() == k2.data_ptr() and k1.stride() == k2.stride()
-    f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=q1.device)
-    g = {"dq1": f(B, H, N, dqk), "dq2": f(B, H, N, dqk), "dk1": f(B, Hkv, N, dqk), "dv": f(B, Hkv, N, dv_),
-         "dlambda": f(H)}
-    g["dk2"] = g["dk1"] if shared else f(B, Hkv, N, dqk)
-    g["dgamma"] = f(H, dv_) if norm else None
     a = BackwardArgs()
     a.dtype = _dtype_code(q1)
     a.B, a.H, a.H_kv, a.N, a.d_qk, a.d_v = B, H, Hkv, N, dqk, dv_
@@ -372,9 +361,39 @@ def backward(q1, q2, k1, k2, v, lam, stats, dout, *, depth: int, causal: bool = 
     a.o1, a.o2, a.lse1, a.lse2 = (_ptr(t) for t in stats)
     a.dout = _ptr(dout)
     a.sdo = _c_int64_3(*_strides3(dout))
-    a.dq1, a.dq2, a.dk1, a.dv, a.dlambda = (_ptr(g[k]) for k in ("dq1", "dq2", "dk1", "dv", "dlambda"))
-    a.dk2 = None if shared else _ptr(g["dk2"])
-    a.dgamma = _ptr(g["dgamma"]) if norm else None
+    if g is not None:
+        a.dq1, a.dq2, a.dk1, a.dv, a.dlambda = (_ptr(g[k]) for k in ("dq1", "dq2", "dk1", "dv", "dlambda"))
+        a.dk2 = None if shared else _ptr(g["dk2"])
+        a.dgamma = _ptr(g["dgamma"]) if norm else None
+    return a
+
+
+def backward_workspace_bytes(q1, q2, k1, k2, v, lam, stats, dout, *, depth: int, causal: bool = True,
+                             norm: bool = False, gamma=None, eps: float = 1e-5, scale: float = 0.0,
+                             window: int = 0) -> int:
+    """Bytes of device workspace backward(...) needs for these arguments."""
+    a = _backward_args(q1, q2, k1, k2, v, lam, stats, dout, None, depth, causal, norm, gamma, eps, scale, window)
+    return int(load_library().diffattn_backward_workspace_bytes(ctypes.byref(a)))
+
+
+def backward(q1, q2, k1, k2, v, lam, stats, dout, *, depth: int, causal: bool = True, norm: bool = False,
+             gamma=None, eps: float = 1e-5, scale: float = 0.0, window: int = 0, workspace=None, stream=None):
+    """Gradients of prefill(q1, q2, k1, k2, v, lam, ...) given dout (bf16
+    [B, H, N, d_v]) and the statistics (o1, o2, lse1, lse2) a prefill call with
+    stats=... stored. Returns a dict of fp32 tensors dq1, dq2, dk1, dk2, dv,
+    dlambda and (norm) dgamma; with k1 is k2 (one key tensor) dk1 is the whole
+    key gradient and dk2 is the same tensor. workspace: None, or a device
+    tensor of at least backward_workspace_bytes(...) bytes, 256-byte aligned."""
+    import torch
+    B, H, N, dqk = q1.shape
+    Hkv, dv_ = k1.shape[1], v.shape[3]
+    shared = k1.data_ptr() == k2.data_ptr() and k1.stride() == k2.stride()
+    f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=q1.device)
+    g = {"dq1": f(B, H, N, dqk), "dq2": f(B, H, N, dqk), "dk1": f(B, Hkv, N, dqk), "dv": f(B, Hkv, N, dv_),
+         "dlambda": f(H)}
+    g["dk2"] = g["dk1"] if shared else f(B, Hkv, N, dqk)
+    g["dgamma"] = f(H, dv_) if norm else None
+    a = _backward_args(q1, q2, k1, k2, v, lam, stats, dout, g, depth, causal, norm, gamma, eps, scale, window)
     lib = load_library()
     need = int(lib.diffattn_backward_workspace_bytes(ctypes.byref(a)))
     if workspace is None:

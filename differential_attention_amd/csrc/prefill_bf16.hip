@@ -401,12 +401,24 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     auto step = [&](auto fast_tag, const unsigned char *base, int sb, bool mask, int lim, int lo) DA_INLINE {
         constexpr bool kFast = decltype(fast_tag)::value;
         const unsigned char *vt = base + T::kNK * T::kKBytes;
-        // every branch's score products first: with two branches per wave the
-        // two product chains interleave, and the rescale test of one branch
-        // (a branch in the code) no longer sits between them
+        // every key fragment of the sub-block is read before the first product
+        // (the reads then overlap each other instead of each product waiting
+        // for its own read); then every branch's score products, so that with
+        // two branches per wave the two product chains interleave
+        bf16x8 kf[NBR][KC];
+#pragma unroll
+        for (int j = 0; j < NBR; ++j)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                kf[j][kc] = as_bf16x8(*(const uint4 *)(base + (SHARED_K ? 0 : (br0 + j) * T::kKBytes) + k_addr(sb, kc)));
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 sc[NBR];
 #pragma unroll
-        for (int j = 0; j < NBR; ++j) sc[j] = qk_branch(base + (SHARED_K ? 0 : (br0 + j) * T::kKBytes), qf[j], sb);
+        for (int j = 0; j < NBR; ++j) {
+            sc[j] = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) sc[j] = mfma32(kf[j][kc], qf[j][kc], sc[j]);
+        }
         bf16x8 pb[NBR][2];
         if constexpr (kFast) {
 #pragma unroll
@@ -420,13 +432,11 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
             for (int j = 0; j < NBR; ++j)
                 softmax_branch(sc[j], mask, lim, lo, m[j], l[j], o[j], pb[j][0], pb[j][1]);
         }
-        // O^T += V^T P^T, one V read for every branch of the wave; the next
-        // step's V operand is read while this step's products run
-        // step i covers (k step t, dv block dc). With one branch per wave the k
-        // step is the outer index, so the 4 accumulators of a k step are updated
-        // back to back and dependent products sit 4 apart; with two branches the
-        // dv block is outer (the two branches' products already alternate), which
-        // keeps the register footprint of the two-branch wave within budget.
+        // O^T += V^T P^T, one V read for every branch of the wave. Step i
+        // covers (k step t, dv block dc). With one branch per wave the k step
+        // is the outer index, so the 4 accumulators of a k step are updated
+        // back to back and dependent products sit 4 apart; with two branches
+        // the dv block is outer (the two branches' products already alternate).
         constexpr bool kStepOuter = NBR == 1;
         auto t_of = [](int i) DA_INLINE { return kStepOuter ? (i >> 2) : (i & 1); };
         auto dc_of = [](int i) DA_INLINE { return kStepOuter ? (i & 3) : (i >> 1); };
@@ -435,14 +445,16 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_addr(sb, t_of(i), dc_of(i), 1)));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        bf16x8 va = vfrag(0);
+        // every value fragment of the sub-block is read before the first
+        // product (the transposing reads overlap each other)
+        bf16x8 vf[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const bf16x8 vn = i + 1 < 8 ? vfrag(i + 1) : va;
+        for (int i = 0; i < 8; ++i) vf[i] = vfrag(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < NBR; ++j) o[j][dc_of(i)] = mfma32(va, pb[j][t_of(i)], o[j][dc_of(i)]);
-            va = vn;
-        }
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < NBR; ++j) o[j][dc_of(i)] = mfma32(vf[i], pb[j][t_of(i)], o[j][dc_of(i)]);
     };
 
     // ---- the key sweep: even tiles in stage 0, odd tiles in stage 1

@@ -32,6 +32,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB: load another build of oracle.c instead (the sanitizer test runs
+# the pins against an AddressSanitizer / UBSan build this way)
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIB")
 _lib = None
 
 
@@ -50,9 +53,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()  # missing, or older than its source (its signatures may have changed)
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()  # missing, or older than its source (its signatures may have changed)
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     i, d, i64 = ctypes.c_int, ctypes.c_double, ctypes.c_int64
     lib.oracle_lambda_init.argtypes = [i]

@@ -8,22 +8,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
-def pytest_addoption(parser):
-    parser.addoption("--runslow", action="store_true", default=False,
-                     help="also run the tests marked slow (all-rows parity of the largest workloads)")
-
-
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; parity tests of the HIP path")
-    config.addinivalue_line("markers", "slow: full-size workloads (minutes of oracle time); run with --runslow")
 
 
 def pytest_collection_modifyitems(config, items):
-    if not config.getoption("--runslow"):
-        skip_slow = pytest.mark.skip(reason="slow: run with --runslow")
-        for item in items:
-            if "slow" in item.keywords:
-                item.add_marker(skip_slow)
     # GPU tests are skipped (not failed) where no GPU is visible, e.g. in the
     # CPU-only build container; on a GPU machine they run.
     try:

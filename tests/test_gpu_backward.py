@@ -2,11 +2,18 @@
 for it) against the fp64 gradient oracle (oracle/backward.py), through the C ABI.
 
 Tolerance for gradients: each gradient tensor's relative Frobenius error
-<= 2e-2 and max |error| <= 5e-2 of its largest magnitude. The path rounds the
+<= 5e-3 and max |error| <= 2e-2 of its largest magnitude. The path rounds the
 output gradient after the norm and the score gradients to bf16 (8 significant
-bits, 2^-9 relative) before the products, as the forward rounds the
-probabilities; accumulation is fp32. dlambda and dgamma (sums over all rows):
-relative error <= 1e-2. The lambda-vector gradients (fp32 only): 1e-5 relative."""
+bits, a relative error of at most 2^-9 = 2.0e-3 per rounding, about 1.1e-3 on
+average) before the products, as the forward rounds the probabilities;
+accumulation is fp32. A gradient element sums many such rounded terms, so
+its error is about one rounding's worth of its size (measured 2.4e-3
+relative Frobenius at most); 5e-3 leaves room for the largest of the
+workloads, and a dropped term or key moves the error far beyond it. The
+stored log-sum-exp must match to 1e-4 of max(1, |lse|): a key dropped from a
+row of N keys moves it by about ln(1 + 1/N) (5e-3 at N 200). dlambda and
+dgamma (sums over all rows): relative error <= 1e-2. The lambda-vector
+gradients (fp32 only): 1e-5 relative."""
 import numpy as np
 import pytest
 
@@ -17,8 +24,9 @@ from oracle import backward as bw
 
 pytestmark = pytest.mark.gpu
 
-GRAD_REL_FRO = 2e-2
-GRAD_MAX_REL = 5e-2
+GRAD_REL_FRO = 5e-3
+GRAD_MAX_REL = 2e-2
+LSE_REL = 1e-4
 
 
 @pytest.fixture(scope="module")
@@ -89,8 +97,10 @@ def test_backward_parity(torch, da, form, N, causal, window):
     check(stats[0].cpu().numpy(), ref["o1"], "bf16", "o1")
     check(stats[1].cpu().numpy(), ref["o2"], "bf16", "o2")
     for k in (2, 3):
-        d = np.abs(stats[k].cpu().numpy() - ref["lse1" if k == 2 else "lse2"]).max()
-        assert d <= 1e-2, ("lse", d)
+        r = ref["lse1" if k == 2 else "lse2"]
+        d = float((np.abs(stats[k].cpu().numpy() - r) / np.maximum(1.0, np.abs(r))).max())
+        say(f"  lse{k - 1}: max relative error {d:.3e}")
+        assert d <= LSE_REL, ("lse", d)
     # with a window of one key each softmax is the constant 1, so the score
     # gradients, and with them dQ and dK, vanish identically (o_k = v_i)
     zs = float(np.abs(ref["dv"]).max()) if window == 1 else None
@@ -180,7 +190,6 @@ def test_backward_group_norm(torch, da, form):
 
 
 # ---------------------------------------------------------------- full-size gradients
-# (minutes of fp64 oracle time; run with --runslow)
 
 
 def _scalar_check(got, ref, what, tol=1e-2):
@@ -191,7 +200,6 @@ def _scalar_check(got, ref, what, tol=1e-2):
     assert err <= tol, (what, err)
 
 
-@pytest.mark.slow
 def test_backward_prefill_v1_all_heads(torch, da):
     # every head of the prefill_v1 shape, and dlambda / dgamma, which sum over
     # all rows of all batches
@@ -224,7 +232,6 @@ def test_backward_prefill_v1_all_heads(torch, da):
     _scalar_check(got["dgamma"], ref["dgamma"], "dgamma")
 
 
-@pytest.mark.slow
 def test_backward_prefill_v2_sampled_heads(torch, da):
     # the prefill_v2 shape (GQA, N 16384): dQ of two heads, and dK, dV of one KV
     # head (the oracle sums its 4 output heads' contributions)

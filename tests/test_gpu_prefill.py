@@ -162,24 +162,27 @@ def test_prefill_v1_full(torch, da):
 
 
 def test_prefill_v2_full(torch, da):
+    # every row of every head: 524288 rows (the oracle over all of them takes
+    # a minute or two on the host's cores, one head at a time)
     p = W.prefill_v2()
     c = PrefillCase(p)
-    say("prefill_v2 full: 64 query heads / 8 KV heads, N 16384, d 128, causal")
-    out = c.run()
-    torch.cuda.synchronize()
-    rows = sampled_rows(p.B, p.H, p.N, seed=22, n_rand=48, edge=16)
-    check(gather_rows(out, rows, p.H, p.N), c.oracle(rows=rows), "bf16", "prefill_v2 sampled rows")
+    say("prefill_v2 full: 64 query heads / 8 KV heads, N 16384, d 128, causal; all rows")
+    out = c.run().float().cpu().numpy()
+    check_all_rows_by_head(c, out, "prefill_v2 all rows")
 
 
 def test_longctx_v1_full(torch, da):
+    # every row of every head (524288 rows, the planted keys' probe rows among
+    # them); the probe rows are also checked on their own
     p = W.longctx_v1()
     c = PrefillCase(p)
-    say("longctx_v1 full: H 8, N 65536, planted keys, causal, RMS")
-    out = c.run()
+    say("longctx_v1 full: H 8, N 65536, planted keys, causal, RMS; all rows")
+    out_d = c.run()
     torch.cuda.synchronize()
-    probe_rows = lambda b, h: np.unique(np.concatenate([p.probes[b, h, :, 0], p.probes[b, h, :, 1]]))
-    rows = sampled_rows(p.B, p.H, p.N, seed=23, n_rand=16, edge=8, extra=probe_rows)
-    check(gather_rows(out, rows, p.H, p.N), c.oracle(rows=rows), "bf16", "longctx_v1 sampled + probe rows")
+    probe = np.unique(np.concatenate([(b * p.H + h) * p.N + p.probes[b, h, :, 1]
+                                      for b in range(p.B) for h in range(p.H)]))
+    check(gather_rows(out_d, probe, p.H, p.N), c.oracle(rows=probe), "bf16", "longctx_v1 probe rows")
+    check_all_rows_by_head(c, out_d.float().cpu().numpy(), "longctx_v1 all rows")
 
 
 # ---------------------------------------------------------------- causal sliding window
@@ -246,28 +249,6 @@ def test_fp32_group_norm(torch, da):
     p.norm = "group"
     c = PrefillCase(p)
     check(c.run().cpu().numpy(), c.oracle(), "f32", "f32 GroupNorm")
-
-
-# ---------------------------------------------------------------- all rows of the largest workloads
-# (minutes of oracle time each: run with --runslow)
-
-
-@pytest.mark.slow
-def test_prefill_v2_all_rows(torch, da):
-    p = W.prefill_v2()
-    c = PrefillCase(p)
-    say("prefill_v2 full: all 524288 rows against the oracle")
-    out = c.run().float().cpu().numpy()
-    check_all_rows_by_head(c, out, "prefill_v2 all rows")
-
-
-@pytest.mark.slow
-def test_longctx_v1_all_rows(torch, da):
-    p = W.longctx_v1()
-    c = PrefillCase(p)
-    say("longctx_v1 full: all 524288 rows against the oracle")
-    out = c.run().float().cpu().numpy()
-    check_all_rows_by_head(c, out, "longctx_v1 all rows")
 
 
 # ---------------------------------------------------------------- score range: exact sweep after the fast one
