@@ -14,6 +14,7 @@ Functions (same names as the C entry points, without the prefix):
   decode_workspace_bytes(...)                    -> int
   decode(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, ...) -> [B, H, d_v]
                                                  (bf16 or fp8 e4m3 KV caches)
+  decode_noalloc(...)                            -> the same, no workspace
   prefill_stats(q1, v)                           -> fp32 buffers for the backward
   backward_workspace_bytes(...)                  -> int
   backward(q1, q2, k1, k2, v, lam, stats, dout, ...) -> dict of gradients
@@ -159,6 +160,8 @@ def load_library(path: Optional[str] = None):
     lib.diffattn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.diffattn_decode.argtypes = [ctypes.POINTER(DecodeArgs), V, ctypes.c_size_t, V]
     lib.diffattn_decode.restype = I
+    lib.diffattn_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), V]
+    lib.diffattn_decode_noalloc.restype = I
     lib.diffattn_backward_workspace_bytes.argtypes = [ctypes.POINTER(BackwardArgs)]
     lib.diffattn_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.diffattn_backward.argtypes = [ctypes.POINTER(BackwardArgs), V, ctypes.c_size_t, V]
@@ -510,4 +513,22 @@ def decode(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int, no
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q1.device)
     _check(lib.diffattn_decode(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_noalloc(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, *, depth: int, norm: bool = False,
+                   gamma=None, eps: float = 1e-5, scale: float = 0.0, out=None, split_pages: int = 0,
+                   dev_err=None, stream=None, k2_cache=None, window: int = 0, k_scale: float = 1.0,
+                   v_scale: float = 1.0):
+    """decode(...) without a workspace: the library's static device scratch
+    holds the partial results (diffattn_decode_noalloc). With out given, no
+    device memory is allocated by this call."""
+    import torch
+    B, H, _ = q1.shape
+    dv = v_cache.shape[3]
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q1.dtype, device=q1.device)
+    a = _decode_args(q1, q2, k_cache, v_cache, page_table, ctx_len, lam, depth, norm, gamma, eps,
+                     scale, out, split_pages, dev_err, k2_cache, window, k_scale, v_scale)
+    _check(load_library().diffattn_decode_noalloc(ctypes.byref(a), _stream(stream)))
     return out

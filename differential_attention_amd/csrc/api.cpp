@@ -86,6 +86,28 @@ int diffattn_decode(const diffattn_decode_args *a, void *workspace, size_t ws_by
     return hip_status(e, "diffattn_decode");
 }
 
+int diffattn_decode_noalloc(const diffattn_decode_args *a, void *stream) {
+    std::string msg;
+    da::DecodePlan plan;
+    int rc = da::check_decode(a, &plan, &msg);
+    if (rc != DIFFATTN_OK) return set_error(rc, msg);
+    if (a->B == 0) {
+        g_last_error.clear();
+        return DIFFATTN_OK;
+    }
+    if (plan.ws_bytes > da::kDecodeScratchBytes)
+        return set_error(DIFFATTN_EWORKSPACE,
+                         "diffattn_decode_noalloc: these arguments need " + std::to_string(plan.ws_bytes) +
+                             " bytes of scratch, more than the " + std::to_string(da::kDecodeScratchBytes) +
+                             " of the static scratch (diffattn_decode takes a workspace of any size)");
+    void *ws = nullptr;
+    hipError_t e = da::decode_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "diffattn_decode_noalloc (scratch lookup)");
+    const float scale = a->scale > 0.0f ? a->scale : (float)(1.0 / sqrt((double)a->d_qk));
+    e = da::launch_decode_bf16(*a, plan, ws, scale, (float)da::lambda_init(a->depth), (hipStream_t)stream);
+    return hip_status(e, "diffattn_decode_noalloc");
+}
+
 size_t diffattn_backward_workspace_bytes(const diffattn_backward_args *a) {
     da::BackwardPlan plan;
     std::string msg;

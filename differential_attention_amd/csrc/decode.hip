@@ -610,4 +610,33 @@ hipError_t launch_decode_bf16(const diffattn_decode_args &a, const DecodePlan &p
     return hipGetLastError();
 }
 
+// ---- static scratch for the allocation-free entry point
+// A file-scope device array: each device that loads the library holds its
+// own copy until the process ends. Host code never uses the array's name as
+// an address (on the host it is only a handle); it uses the device address
+// hipGetSymbolAddress returns for the current device, looked up on the first
+// call on that device and kept per device. Every call on one device shares
+// this array: its contents need no initialisation (the split pass writes
+// every record the combine pass reads), and calls that overlap on one device
+// race.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void *> addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);  // racing first calls store the same address
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 }  // namespace da

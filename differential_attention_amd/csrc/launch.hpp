@@ -28,4 +28,8 @@ hipError_t launch_lambda_backward(const float *lq1, const float *lk1, const floa
 hipError_t launch_decode_bf16(const diffattn_decode_args &a, const DecodePlan &plan, void *workspace,
                               float scale, float lambda_init, hipStream_t stream);
 
+// Device address of the current device's static decode scratch
+// (kDecodeScratchBytes), looked up once per device.
+hipError_t decode_scratch(void **ptr);
+
 }  // namespace da

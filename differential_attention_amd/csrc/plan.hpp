@@ -22,6 +22,9 @@ namespace da {
 constexpr int kDecodeMaxWgs = 2048;   // work-groups of the split pass, at most
 constexpr int kDecodeMinPages = 4;    // pages per work-group, at least (library's choice)
 constexpr int kDecodeMaxTarget = 1 << 24;
+// Bytes of the static device scratch diffattn_decode_noalloc uses in place of
+// a workspace (one array per device, for the life of the process).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
 
 struct DecodePlan {
     int target_pages = 0;      // pages per work-group asked for; 0 = library's choice

@@ -31,8 +31,9 @@
  *  - DIFFATTN_EHIP means a launch was attempted and the HIP runtime reported
  *    an error (for example, no device); outputs are then undefined.
  *  - The library holds no state between calls apart from a per-device
- *    cache of the compute-unit count and kernel occupancy, and is safe to
- *    call from several host threads (the last-error message is thread-local).
+ *    cache of the compute-unit count and kernel occupancy and the static
+ *    scratch of diffattn_decode_noalloc, and is safe to call from several
+ *    host threads (the last-error message is thread-local).
  */
 #ifndef DIFFATTN_H
 #define DIFFATTN_H
@@ -192,6 +193,24 @@ size_t diffattn_decode_workspace_bytes(const diffattn_decode_args *a);
  * workspace must be ordered on one stream.
  */
 int diffattn_decode(const diffattn_decode_args *a, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Paged decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Same arguments, kernels and results as diffattn_decode;
+ * the split-KV partial results go to a static device scratch of 32 MiB
+ * (each device the library runs on holds its own until the process ends)
+ * instead of a caller workspace. Allocates nothing and calls no allocating
+ * routine. Returns DIFFATTN_EWORKSPACE, launching nothing, when the
+ * arguments need more scratch than that (diffattn_decode_workspace_bytes(a)
+ * > 32 MiB; the need is a small header plus at most 2048 + B * H_kv records
+ * of 2 * (H / H_kv) * (d_v + 2) fp32 each, so with 4 query pairs per KV head
+ * up to about 6000 (sequence, KV head) pairs fit). All calls on one device
+ * share the scratch, which keeps the last call's contents and needs no
+ * clearing: calls that overlap on one device (different streams, or host
+ * threads without ordering) race; calls ordered on one stream do not.
+ */
+int diffattn_decode_noalloc(const diffattn_decode_args *a, void *stream);
 
 /*
  * Backward pass of the prefill (the gradients of the function defined above;

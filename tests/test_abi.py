@@ -236,6 +236,22 @@ def test_decode_rejects_small_workspace(lib):
     assert lib.diffattn_decode(ctypes.byref(a), None, need, None) == da.EWORKSPACE
 
 
+def test_decode_noalloc_checks_before_any_launch(lib):
+    # the argument checks are those of diffattn_decode; a request needing more
+    # than the 32 MiB static scratch is refused before any device call
+    a = _decode_args(B=0)
+    assert lib.diffattn_decode_noalloc(ctypes.byref(a), None) == da.OK
+    a = _decode_args(sq1=(ctypes.c_int64 * 2)(64 * 128, 7))
+    assert lib.diffattn_decode_noalloc(ctypes.byref(a), None) == da.EINVAL
+    a = _decode_args(B=4096, H=64, max_pages=1,
+                     sq1=(ctypes.c_int64 * 2)(64 * 128, 128), sq2=(ctypes.c_int64 * 2)(64 * 128, 128),
+                     so=(ctypes.c_int64 * 2)(64 * 128, 128))
+    need = lib.diffattn_decode_workspace_bytes(ctypes.byref(a))
+    assert need > 32 << 20
+    assert lib.diffattn_decode_noalloc(ctypes.byref(a), None) == da.EWORKSPACE
+    assert "scratch" in lib.diffattn_last_error().decode()
+
+
 def test_lambda_rejects(lib):
     f = lib.diffattn_lambda
     assert f(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, 0, 8, 1, FAKE + 65536, None) == da.EINVAL
