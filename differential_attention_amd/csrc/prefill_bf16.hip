@@ -103,12 +103,13 @@ struct Bf16Params {
     float *o1, *o2, *lse1, *lse2;  // optional statistics for the backward pass (all or none)
     int B, H, H_kv, group, N, causal, window, row_blocks, xcd_units;
     int group_norm;  // the norm subtracts the channel mean first (GroupNorm per head)
-    int prescale;    // the fixed-reference sweep is allowed (off when statistics are stored)
     float sc_log2;  // scale * log2(e)
     float eps, one_minus_init;
 };
 
-template <int DQK, bool SHARED_K, bool NORM, bool WIN>
+// STATS: also store each branch's normalised output and log-sum-exp for the
+// backward pass (o1, o2, lse1, lse2); such calls take the exact sweep only.
+template <int DQK, bool SHARED_K, bool NORM, bool WIN, bool STATS>
 __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void prefill_bf16_kernel(Bf16Params p) {
     using T = Tile<DQK, SHARED_K>;
     using S = Split<DQK>;
@@ -192,15 +193,16 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     //    whose two branches nearly cancel, the V1 norm magnifies any error);
     //  * the scores of 32 keys every row sees (sampled before the sweep) span
     //    at most kFastMaxRange in every row.
-    // Neither holds with stored statistics (the backward recomputes the exact
-    // scores) and neither is needed for the result to be right: the exact
-    // sweep is always available.
+    // Calls that store statistics always take the exact sweep (the backward
+    // recomputes the exact scores against the stored log-sum-exp). Neither
+    // test is needed for the result to be right: the exact sweep is always
+    // available.
     const int min_keys = WIN ? min(p.causal ? q0 + 1 : p.N, p.window) : (p.causal ? q0 + 1 : p.N);
     // first sampled key: the window start of the work-group's last row, so
     // that keys ks .. ks+31 are visible to every row (a window that cuts no
     // row's keys samples the same keys as no window)
     const int ks = WIN ? max(0, min(q0 + S::kBM, p.N) - p.window) : 0;
-    bool fast = p.prescale && min_keys >= kFastMinKeys && ks + 31 <= (p.causal ? q0 : p.N - 1);
+    bool fast = !STATS && min_keys >= kFastMinKeys && ks + 31 <= (p.causal ? q0 : p.N - 1);
     float scl = p.sc_log2;  // multiplier from the products' scores to log2 units
     if (fast) {  // work-group-uniform
 #pragma unroll
@@ -290,14 +292,18 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     };
 
     // ---- online-softmax state of this wave's branches
+    // l sums the bf16-rounded probabilities the value products use (so the
+    // output's weights sum to one); le (statistics only) sums them unrounded,
+    // for the log-sum-exp
     f32x16 o[NBR][4];
-    float m[NBR], l[NBR];
+    float m[NBR], l[NBR], le[NBR];
 #pragma unroll
     for (int j = 0; j < NBR; ++j) {
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) o[j][dc] = f32x16{};
         m[j] = -INFINITY;
         l[j] = 0.0f;
+        le[j] = 0.0f;
     }
 
     // byte offset of this lane's K-operand chunk for k step kc, sub-block sb
@@ -319,17 +325,10 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     };
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // scores S^T = K Q^T of one branch for one sub-block
-    auto qk_branch = [&](const unsigned char *kt, const bf16x8 *q, int sb) DA_INLINE {
-        f32x16 s = f32x16{};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) s = mfma32(as_bf16x8(*(const uint4 *)(kt + k_addr(sb, kc))), q[kc], s);
-        return s;
-    };
     // online softmax of one branch's scores (reference max moved lazily), bf16
     // probabilities for the two 16-key steps
-    auto softmax_branch = [&](f32x16 s, bool mask, int lim, int lo, float &mr, float &lr, f32x16 *orr, bf16x8 &pb0,
-                              bf16x8 &pb1) DA_INLINE {
+    auto softmax_branch = [&](f32x16 s, bool mask, int lim, int lo, float &mr, float &lr, float &er, f32x16 *orr,
+                              bf16x8 &pb0, bf16x8 &pb1) DA_INLINE {
         if (mask) {
             // an opaque statement keeps this a branch taken by the few masked
             // sub-blocks, instead of per-element selects evaluated for all
@@ -348,12 +347,22 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
             const float alpha = (mr == mnew) ? 1.0f : exp2_fast(mr - mnew);
             mr = mnew;
             lr *= alpha;
+            if constexpr (STATS) er *= alpha;
 #pragma unroll
             for (int dc = 0; dc < 4; ++dc) orr[dc] *= alpha;
         }
         const float msub = (mr == -INFINITY) ? 0.0f : mr;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = exp2_fast(fmaf(s[r], scl, -msub));
+        if constexpr (STATS) {
+            float e0 = s[0] + s[1], e1 = s[2] + s[3];
+#pragma unroll
+            for (int r = 4; r < 16; r += 4) {
+                e0 += s[r] + s[r + 1];
+                e1 += s[r + 2] + s[r + 3];
+            }
+            er += e0 + e1;
+        }
         bf16x2 pp[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) pp[i] = pack2(s[2 * i], s[2 * i + 1]);
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
         } else {
 #pragma unroll
             for (int j = 0; j < NBR; ++j)
-                softmax_branch(sc[j], mask, lim, lo, m[j], l[j], o[j], pb[j][0], pb[j][1]);
+                softmax_branch(sc[j], mask, lim, lo, m[j], l[j], le[j], o[j], pb[j][0], pb[j][1]);
         }
         // O^T += V^T P^T, one V read for every branch of the wave. Step i
         // covers (k step t, dv block dc). With one branch per wave the k step
@@ -546,6 +555,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
                 for (int dc = 0; dc < 4; ++dc) o[j][dc] = f32x16{};
                 m[j] = -INFINITY;
                 l[j] = 0.0f;
+                le[j] = 0.0f;
             }
             load_q();  // the exact sweep takes the exact queries
             scl = p.sc_log2;
@@ -558,10 +568,13 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
 
     // ---- epilogue: y = O1 / l1 - lambda O2 / l2 (then the V1 norm), bf16 store
 #pragma unroll
-    for (int j = 0; j < NBR; ++j) l[j] = halves_sum(l[j]);
+    for (int j = 0; j < NBR; ++j) {
+        l[j] = halves_sum(l[j]);
+        if constexpr (STATS) le[j] = halves_sum(le[j]);
+    }
     // statistics for the backward pass: each branch's normalised output and
     // natural-log log-sum-exp of its scaled scores (m is in log2 units)
-    if (p.o1 && myrow < p.N) {
+    if (STATS && myrow < p.N) {
         const int64_t rowid = ((int64_t)b * p.H + h) * p.N + myrow;
 #pragma unroll
         for (int j = 0; j < NBR; ++j) {
@@ -576,7 +589,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
                                        o[j][dc][4 * rq + 3] * rl};
                     *(float4 *)(ob + 32 * dc + 8 * rq) = v4;
                 }
-            if (hh == 0) (brj ? p.lse2 : p.lse1)[rowid] = (m[j] + log2f(l[j])) * 0.69314718055994531f;
+            if (hh == 0) (brj ? p.lse2 : p.lse1)[rowid] = (m[j] + log2f(le[j])) * 0.69314718055994531f;
         }
     }
     f32x16 y[4];
@@ -666,15 +679,21 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     }
 }
 
-template <int DQK, bool SHARED_K, bool NORM>
-hipError_t launch_t(const Bf16Params &p, int blocks, hipStream_t stream) {
+template <int DQK, bool SHARED_K, bool NORM, bool STATS>
+hipError_t launch_s(const Bf16Params &p, int blocks, hipStream_t stream) {
     if (p.window > 0)
-        hipLaunchKernelGGL((prefill_bf16_kernel<DQK, SHARED_K, NORM, true>), dim3(blocks),
+        hipLaunchKernelGGL((prefill_bf16_kernel<DQK, SHARED_K, NORM, true, STATS>), dim3(blocks),
                            dim3(Split<DQK>::kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_bf16_kernel<DQK, SHARED_K, NORM, false>), dim3(blocks),
+        hipLaunchKernelGGL((prefill_bf16_kernel<DQK, SHARED_K, NORM, false, STATS>), dim3(blocks),
                            dim3(Split<DQK>::kThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int DQK, bool SHARED_K, bool NORM>
+hipError_t launch_t(const Bf16Params &p, int blocks, hipStream_t stream) {
+    return p.o1 ? launch_s<DQK, SHARED_K, NORM, true>(p, blocks, stream)
+                : launch_s<DQK, SHARED_K, NORM, false>(p, blocks, stream);
 }
 
 }  // namespace
@@ -714,7 +733,6 @@ hipError_t launch_prefill_bf16(const diffattn_prefill_args &a, float scale, floa
     const int kv_units = a.B * a.H_kv;
     p.xcd_units = (kv_units % 8 == 0) ? kv_units / 8 : 0;
     p.sc_log2 = scale * kLog2e;
-    p.prescale = a.o1 == nullptr;  // the statistics for the backward keep the exact scores
     p.eps = a.eps;
     p.one_minus_init = 1.0f - lambda_init;
     const int64_t blocks = (int64_t)a.B * a.H * p.row_blocks;

@@ -10,6 +10,8 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; parity tests of the HIP path")
+    import gpu_util
+    gpu_util._PYTEST_CONFIG = config  # live progress lines of the minutes-long checks
 
 
 def pytest_collection_modifyitems(config, items):

@@ -15,9 +15,19 @@ BF16_REL_FRO = 1e-2
 F32_MAX_ABS = 1e-5
 
 
-def say(msg: str):
+_PYTEST_CONFIG = None  # set by conftest.py: lets say(..., live=True) bypass output capture
+
+
+def say(msg: str, live: bool = False):
+    """Print a progress line (kept with the test's captured output). live:
+    also write it straight to the terminal while the test runs, so that a
+    check lasting minutes shows its progress as it goes."""
     print(msg, flush=True)
     sys.stdout.flush()
+    cm = _PYTEST_CONFIG.pluginmanager.getplugin("capturemanager") if live and _PYTEST_CONFIG else None
+    if cm is not None:
+        with cm.global_and_fixture_disabled():
+            print(msg, flush=True)
 
 
 def dev():
@@ -68,7 +78,7 @@ def check_all_rows_by_head(c, out, what: str):
             mx = max(mx, float(np.abs(diff).max()))
             dd += float((diff * diff).sum())
             rr += float((ref * ref).sum())
-            say(f"  {what}: batch {b} head {h} done, max|d| so far {mx:.3e}")
+            say(f"  {what}: batch {b} head {h} done, max|d| so far {mx:.3e}", live=True)
     fro = (dd / max(rr, 1e-300)) ** 0.5
     say(f"  {what}: max|d| {mx:.3e} rel-fro {fro:.3e} over {out.size} elements")
     assert mx <= BF16_MAX_ABS, f"{what}: max abs error {mx}"
