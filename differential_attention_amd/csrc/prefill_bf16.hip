@@ -103,6 +103,7 @@ struct Bf16Params {
     float *o1, *o2, *lse1, *lse2;  // optional statistics for the backward pass (all or none)
     int B, H, H_kv, group, N, causal, window, row_blocks, xcd_units;
     int group_norm;  // the norm subtracts the channel mean first (GroupNorm per head)
+    int off32;       // each (batch, KV head) slice of K1, K2 and V spans fewer than 2^31 bytes
     float sc_log2;  // scale * log2(e)
     float eps, one_minus_init;
 };
@@ -267,10 +268,56 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     // hold the K tile(s), the rest the V tile. Slot -> (row, physical chunk)
     // -> logical chunk through the row's swizzle.
     static_assert(T::kBlocks % NW == 0, "stage blocks must divide among the waves");
+    static_assert((T::kKBytes / 1024) % NW == 0, "a wave's copy i reads one tensor, fixed by i");
+    constexpr int NC = T::kBlocks / NW;  // copies per wave and tile
+    constexpr int KPB = T::kKBytes / 1024 / NW;  // copies per K tile
+    const int wv = wave_id();            // the wave index as a scalar
+    // With off32, a whole tile in range is copied by buffer loads: the
+    // (batch, KV head) slice's base in a buffer descriptor, a scalar offset
+    // (the tile's first key, and the copy's first row inside the tile, times
+    // the row stride) and one per-lane offset per tensor, so a tile costs no
+    // vector arithmetic. The copies of one tensor differ only by whole rows
+    // (NW blocks apart: a multiple of every swizzle's period), so one lane
+    // offset serves them all; K1 and K2 share theirs (off32 requires equal
+    // row strides). The last, partial tile (rows clamped to the last key) and
+    // huge strides take the general form below.
+    constexpr int KRows = NW * T::kRowsPerKBlock;  // rows between a wave's consecutive K copies
+    constexpr int VRows = NW * 4;                  // and between its V copies (4 rows a block)
+    static_assert(KRows % 16 == 0 && VRows % 4 == 0, "copy row steps must keep the swizzles");
+    uint32_t koff, voff;
+    {
+        const int krow = wv * T::kRowsPerKBlock + lane / T::kKCh;
+        koff = 2u * (uint32_t)(krow * sk1n + 8 * ((lane % T::kKCh) ^ k_swz<DQK>(krow)));
+        const int vrow = wv * 4 + (lane >> 4);
+        voff = 2u * (uint32_t)(vrow * svn + 8 * ((lane & 15) ^ v_swz(vrow)));
+    }
+    // raw buffer descriptors (stride 0, 32-bit data format: dword 3 =
+    // 0x00020000) over the three slices; range 2^31 - 1 bytes (off32)
+    const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc((void *)kb1, (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc((void *)kb2, (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, 0x7fffffff, 0x00020000);
     auto issue_tile = [&](int t, unsigned char *base) DA_INLINE {
-        const int key0 = t * kBN;
+        const int key0 = __builtin_amdgcn_readfirstlane(t * kBN);  // uniform: keeps the offsets scalar
+        if (p.off32 && key0 + kBN <= p.N) {
 #pragma unroll
-        for (int i = 0; i < T::kBlocks / NW; ++i) {
+            for (int i = 0; i < NC; ++i) {
+                const int blk = wv + NW * i;
+                if (i < T::kNK * KPB) {
+                    const int kt = i / KPB, j = i % KPB;  // tensor, and copy inside it
+                    const uint32_t so = 2u * (uint32_t)(key0 + j * KRows) * (uint32_t)sk1n;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(kt ? rk2 : rk1, (lds_void *)(base + blk * 1024), 16,
+                                                             koff, so, 0, 0);
+                } else {
+                    const int j = i - T::kNK * KPB;
+                    const uint32_t so = 2u * (uint32_t)(key0 + j * VRows) * (uint32_t)svn;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(base + blk * 1024), 16, voff, so, 0,
+                                                             0);
+                }
+            }
+        return;
+        }
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
             const int blk = wave + NW * i;
             if (blk < T::kKBlocks) {
                 const int kt = blk / (T::kKBytes / 1024);  // which K tile (0: K1, 1: K2)
@@ -740,6 +787,15 @@ hipError_t launch_prefill_bf16(const diffattn_prefill_args &a, float scale, floa
     const bool shared = a.k1 == a.k2 && a.sk1[0] == a.sk2[0] && a.sk1[1] == a.sk2[1] && a.sk1[2] == a.sk2[2];
     const bool norm = a.norm != DIFFATTN_NORM_NONE;
     p.group_norm = a.norm == DIFFATTN_NORM_GROUP;
+    {
+        // bytes from a slice's first row to the end of its last: the buffer
+        // offsets (scalar tile offset + per-lane offset) stay below 2^31
+        const int64_t n1 = std::max<int64_t>(a.N - 1, 63);
+        int64_t most = a.sv[2] * n1 + a.d_v;
+        most = std::max(most, a.sk1[2] * n1 + a.d_qk);
+        most = std::max(most, a.sk2[2] * n1 + a.d_qk);
+        p.off32 = 2 * most <= INT32_MAX && a.sk1[2] == a.sk2[2];
+    }
     const int nb = (int)blocks;
     if (a.d_qk == 64) {
         if (shared) return norm ? launch_t<64, true, true>(p, nb, stream) : launch_t<64, true, false>(p, nb, stream);
