@@ -56,6 +56,8 @@ struct BwdParams {
     float *dt1, *dt2;  // workspace: rowsum(dy * o_k), [B, H, N]
     float *part;       // workspace: per prep block [dlambda, dgamma[128]]
     int B, H, H_kv, group, N, causal, window, norm, prep_nblk, row_blocks, key_blocks;
+    int qoff32;  // Q1 and Q2 share their strides and one batch of each spans fewer than 2^31 bytes
+    int koff32;  // K1 and K2 share their row stride and each (batch, KV head) slice of K1, K2, V spans < 2^31 bytes
     float scale, sc_log2, eps, one_minus_init;
 };
 
@@ -215,8 +217,46 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     const int nsub = wrow0 < p.N ? (wend + 31) / 32 : 0;
 
     static_assert(T::kBlocks % NW == 0, "stage blocks must divide among the waves");
+    // With koff32, a tile wholly inside the sequence is copied by buffer
+    // loads (descriptors over this (batch, KV head) slice, the tile's first
+    // row times the stride as a scalar offset, one per-lane offset per tensor:
+    // a wave's copies of one tensor are whole swizzle periods apart, and K1
+    // and K2 share their strides); the last, partial tile and huge strides
+    // take the general form.
+    static_assert((T::kKBytes / 1024) % NW == 0, "copy i reads one tensor, fixed by i");
+    constexpr int KPB = T::kKBytes / 1024 / NW;
+    constexpr int KRows = NW * T::kRowsPerKBlock, VRows = NW * 4;
+    static_assert(KRows % 16 == 0 && VRows % 16 == 0, "copy row steps must keep the swizzles");
+    const int wv = wave_id();
+    uint32_t koff, voff;
+    {
+        const int kr = wv * T::kRowsPerKBlock + lane / T::kKCh;
+        koff = 2u * (uint32_t)(kr * sk1n + 8 * ((lane % T::kKCh) ^ bk_swz<DQK>(kr)));
+        const int vr = wv * 4 + (lane >> 4);
+        voff = 2u * (uint32_t)(vr * svn + 8 * ((lane & 15) ^ bv_swz(vr)));
+    }
+    const __amdgpu_buffer_rsrc_t rk1 = __builtin_amdgcn_make_buffer_rsrc((void *)kb1, (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk2 = __builtin_amdgcn_make_buffer_rsrc((void *)kb2, (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, 0x7fffffff, 0x00020000);
     auto issue_tile = [&](int t, unsigned char *base) DA_INLINE {
-        const int key0 = t * kBN;
+        const int key0 = __builtin_amdgcn_readfirstlane(t * kBN);
+        if (p.koff32 && key0 + kBN <= p.N) {
+#pragma unroll
+            for (int i = 0; i < T::kBlocks / NW; ++i) {
+                const int blk = wv + NW * i;
+                if (i < T::kNK * KPB) {
+                    const int j = i % KPB;
+                    const uint32_t so = 2u * (uint32_t)(key0 + j * KRows) * (uint32_t)sk1n;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(i < KPB ? rk1 : rk2, (lds_void *)(base + blk * 1024), 16,
+                                                             koff, so, 0, 0);
+                } else {
+                    const int j = i - T::kNK * KPB;
+                    const uint32_t so = 2u * (uint32_t)(key0 + j * VRows) * (uint32_t)svn;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(base + blk * 1024), 16, voff, so, 0, 0);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < T::kBlocks / NW; ++i) {
             const int blk = wave + NW * i;
@@ -393,11 +433,61 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         return tlo + nt - 1 - tt;
     };
 
+    // With qoff32, a tile wholly inside the sequence is copied by buffer
+    // loads: one descriptor per tensor over this batch, the head and first
+    // row (times the strides) as a scalar offset and one per-lane offset per
+    // tensor; a wave's copies of one tensor are whole 16-row steps apart (the
+    // swizzles' period), so Q1 and Q2 share one lane offset and dy has one.
+    // The tile holding the end of the sequence (rows clamped) and huge
+    // strides take the general form.
+    static_assert((kQBytes / 1024) % NW == 0 && (kDBytes / 1024) % NW == 0, "copy i reads one tensor, fixed by i");
+    constexpr int QPB = kQBytes / 1024 / NW;        // a wave's copies per Q tile
+    constexpr int QRows = NW * kRowsPerQBlock;      // rows between them
+    constexpr int DRows = NW * 4;                   // rows between a wave's dy copies
+    static_assert(QRows % 16 == 0 && DRows % 16 == 0, "copy row steps must keep the swizzles");
+    uint32_t qoff, doff;
+    {
+        const int qr = wave * kRowsPerQBlock + lane / kQCh;
+        qoff = 2u * (uint32_t)(qr * p.sq1[2] + 8 * ((lane % kQCh) ^ bk_swz<DQK>(qr)));
+        const int dr = wave * 4 + (lane >> 4);
+        doff = 2u * (uint32_t)(dr * kDV + 8 * ((lane & 15) ^ bv_swz(dr)));
+    }
+    // raw buffer descriptors (stride 0, 32-bit data format: dword 3 = 0x00020000)
+    const __amdgpu_buffer_rsrc_t rq1 =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(p.q1 + b * p.sq1[0]), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq2 =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(p.q2 + b * p.sq2[0]), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.dy + (int64_t)b * p.H * p.N * kDV), (short)0, 0x7fffffff, 0x00020000);
+    const float *stat_arr = wave == 0 ? p.lse1 : wave == 1 ? p.lse2 : wave == 2 ? p.dt1 : p.dt2;
+    const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(stat_arr + (int64_t)b * p.H * p.N), (short)0, 0x7fffffff, 0x00020000);
+
     auto issue_tile = [&](int x, unsigned char *base) DA_INLINE {
         int hg;
         const int t = tile_of(x, hg);
         const int h = g * p.group + hg;
         const int r0 = t * kBN;
+        if (p.qoff32 && r0 + kBN <= p.N) {
+            const int hs = __builtin_amdgcn_readfirstlane(h), rs = __builtin_amdgcn_readfirstlane(r0);
+#pragma unroll
+            for (int i = 0; i < kBlocks / NW; ++i) {
+                const int blk = wave + NW * i;
+                if (i < 2 * QPB) {
+                    const int j = i % QPB;
+                    const uint32_t so = 2u * (uint32_t)(hs * p.sq1[1] + (rs + j * QRows) * p.sq1[2]);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(i < QPB ? rq1 : rq2, (lds_void *)(base + blk * 1024), 16,
+                                                             qoff, so, 0, 0);
+                } else {
+                    const int j = i - 2 * QPB;
+                    const uint32_t so = 2u * (uint32_t)((hs * p.N + rs + j * DRows) * kDV);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdy, (lds_void *)(base + blk * 1024), 16, doff, so, 0, 0);
+                }
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rst, (lds_void *)(base + kBlocks * 1024 + wave * 256), 4,
+                                                     4u * (uint32_t)lane, 4u * (uint32_t)(hs * p.N + rs), 0, 0);
+            return;
+        }
         const __bf16 *qb1 = p.q1 + b * p.sq1[0] + h * p.sq1[1];
         const __bf16 *qb2 = p.q2 + b * p.sq2[0] + h * p.sq2[1];
         const __bf16 *db = p.dy + ((int64_t)b * p.H + h) * p.N * kDV;
@@ -752,6 +842,17 @@ hipError_t launch_backward_bf16(const diffattn_backward_args &a, const BackwardP
     p.prep_nblk = (a.N + kBwdPrepRows - 1) / kBwdPrepRows;
     p.row_blocks = (a.N + kBM - 1) / kBM;
     p.key_blocks = (a.N + kKB - 1) / kKB;
+    {
+        // the buffer-load copies keep every offset inside one batch below 2^31
+        // bytes: Q1 and Q2 (equal strides), dy (bf16, [H, N, 128]) and the
+        // fp32 statistics ([H, N])
+        const int64_t qmost = a.sq1[1] * (a.H - 1) + a.sq1[2] * (a.N - 1) + a.d_qk;
+        const bool same = a.sq1[1] == a.sq2[1] && a.sq1[2] == a.sq2[2];
+        p.qoff32 = same && 2 * qmost <= INT32_MAX && (int64_t)a.H * a.N * kDV * 2 <= INT32_MAX;
+        const int64_t n1 = std::max<int64_t>(a.N - 1, 63);
+        const int64_t kmost = std::max(std::max(a.sk1[2], a.sk2[2]) * n1 + a.d_qk, a.sv[2] * n1 + kDV);
+        p.koff32 = a.sk1[2] == a.sk2[2] && 2 * kmost <= INT32_MAX;
+    }
     p.scale = scale;
     p.sc_log2 = scale * kLog2e;
     p.eps = a.eps;
