@@ -478,7 +478,7 @@ def main():
         ms = a.elapsed_time(b) / n_calls
         Fw = prefill_flops(w.B, w.H, w.N, w.d_qk, w.d_v)
         ach = Fw / (ms * 1e-3) / 1e12
-        kern = f"prefill_bf16_kernel<{w.d_qk}, {'true' if w.shared_k else 'false'}, {'true' if w.norm else 'false'}, false>"
+        kern = f"prefill_bf16_kernel<{w.d_qk}, {'true' if w.shared_k else 'false'}, {'true' if w.norm else 'false'}, false, false>"
         other[w.name] = {"value": ach, "unit": "TFLOP/s", "ms_per_call": ms, "calls": n_calls,
                          "workload": describe(w),
                          "roofline": {"bound": "mfma", "kernel": kern, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
@@ -504,7 +504,7 @@ def main():
     if args.only != "decode":
         line["value"] = F / (res["prefill_part_ms"] * 1e-3) / 1e12
         ach = F / (res["prefill_kernel_ms"] * 1e-3) / 1e12
-        line["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<64, false, true, false>",
+        line["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<64, false, true, false, false>",
                             "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": ach / BF16_PEAK_TFLOPS, "traffic": load_traffic(p.name)}
     if d is not None:
