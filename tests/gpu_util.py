@@ -80,7 +80,7 @@ def check_all_rows_by_head(c, out, what: str):
             rr += float((ref * ref).sum())
             say(f"  {what}: batch {b} head {h} done, max|d| so far {mx:.3e}", live=True)
     fro = (dd / max(rr, 1e-300)) ** 0.5
-    say(f"  {what}: max|d| {mx:.3e} rel-fro {fro:.3e} over {out.size} elements")
+    say(f"  {what}: max|d| {mx:.3e} rel-fro {fro:.3e} over {out.size} elements", live=True)
     assert mx <= BF16_MAX_ABS, f"{what}: max abs error {mx}"
     assert fro <= BF16_REL_FRO, f"{what}: relative Frobenius error {fro}"
 

@@ -144,6 +144,32 @@ def test_backward_is_deterministic(torch, da):
             assert torch.equal(g1[k], g2[k]), k
 
 
+def test_backward_general_copy_paths_are_bitwise_equal(torch, da):
+    # Both backward kernels copy whole tiles with buffer loads when the two
+    # query (or key) tensors share their strides; otherwise every tile goes
+    # through per-lane addresses. Same bytes in LDS: bitwise-equal gradients.
+    p = _case("v1", 300, True, seed=23)
+    c = PrefillCase(p)
+    stats = da.prefill_stats(c.q1, c.v)
+    c.run(stats=stats)
+    rng = np.random.default_rng(23)
+    dout = to_dev(W.f32_to_bf16(rng.standard_normal((p.B, p.H, p.N, p.d_v)).astype(np.float32)), "bf16")
+    kw = dict(depth=p.depth, causal=True, norm=True, gamma=c.gamma, eps=p.eps)
+    g1 = da.backward(c.q1, c.q2, c.k1, c.k2, c.v, c.lam, stats, dout, **kw)
+    g1 = {k: (x.clone() if x is not None else None) for k, x in g1.items()}
+
+    def wide(x, extra=64):
+        w = torch.zeros(x.shape[:3] + (x.shape[3] + extra,), dtype=x.dtype, device=x.device)
+        w[..., :x.shape[3]] = x
+        return w[..., :x.shape[3]]
+
+    say("backward V1, N 300: Q2 and K2 rows 64 elements longer than Q1's and K1's")
+    g2 = da.backward(c.q1, wide(c.q2), c.k1, wide(c.k2), c.v, c.lam, stats, dout, **kw)
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g1[k], g2[k]), k
+
+
 def test_lambda_backward(torch, da):
     rng = np.random.default_rng(3)
     H, dl = 5, 64

@@ -115,6 +115,39 @@ def test_bf16_explicit_scale_and_strided_out(torch, da):
 
 # ---------------------------------------------------------------- invariants (bitwise)
 
+def _wide_rows(torch, x, extra):
+    """The same values as x [B, H, N, d], in a view whose rows are `extra`
+    elements longer (a different row stride)."""
+    w = torch.zeros(x.shape[:3] + (x.shape[3] + extra,), dtype=x.dtype, device=x.device)
+    w[..., :x.shape[3]] = x
+    return w[..., :x.shape[3]]
+
+
+def test_bf16_general_copy_path_is_bitwise_equal(torch, da):
+    # Whole key/value tiles are copied with buffer loads when K1 and K2 share
+    # their row stride and every (batch, KV head) slice spans less than 2^31
+    # bytes; other layouts copy every tile through per-lane addresses. Both
+    # must fill LDS with the same bytes, so the outputs agree bit for bit.
+    c = PrefillCase(_bf16_case("v1", 700, True, B=1, seed=21))
+    say("V1, N 700: K2 rows 64 elements longer than K1's")
+    a = c.run().clone()
+    c.k2 = _wide_rows(torch, c.k2, 64)
+    assert torch.equal(a, c.run())
+    # V2 with shared keys: a value row stride of 2^21 elements, so one slice
+    # of V spans 2.5 GB (the storage is allocated, only 128 elements a row are set)
+    p = W.prefill_v2(seed=22, B=1, H=2, H_kv=1, N=600)
+    c = PrefillCase(p)
+    say("V2, N 600: value rows 2^21 elements apart")
+    a = c.run().clone()
+    rs = 1 << 21
+    store = torch.empty(p.N * rs, dtype=torch.bfloat16, device=dev())
+    v = store.as_strided((1, 1, p.N, p.d_v), (p.N * rs, p.N * rs, rs, 1))
+    v.copy_(c.v)
+    c.v = v
+    assert torch.equal(a, c.run())
+    del store, v
+
+
 def test_lambda_zero_ignores_branch_two(torch, da):
     c = PrefillCase(_bf16_case("v1", 190, True, B=1, seed=11))
     zero = torch.zeros(c.p.H, dtype=torch.float32, device=dev())
