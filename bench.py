@@ -273,7 +273,14 @@ def single_workload(args, torch, da, W, dev):
         if win:
             desc += f", causal window {win}"
     else:
-        p = getattr(W, name)()
+        if name == "copy_lds":
+            # every key/value byte read once, by one work-group, through the
+            # LDS-DMA buffer loads: a non-causal V1 prefill with one 192-row
+            # block per head (no sharing between work-groups, no fast-sweep
+            # sample since rows see fewer than 256 keys), 256 heads
+            p = W.prefill_v1(seed=31, B=4, H=64, N=192, causal=False)
+        else:
+            p = getattr(W, name)()
         dt = p.dtype
         if p.q_full is not None:
             qf = to_dev(p.q_full, dt)
@@ -290,6 +297,8 @@ def single_workload(args, torch, da, W, dev):
         call = lambda: da.prefill(q1, q2, k1, k2, v, lam, depth=p.depth, causal=p.causal, norm=p.norm,
                                   gamma=gamma, eps=p.eps, out=out, window=win)
         work = prefill_flops(p.B, p.H, p.N, p.d_qk, p.d_v, win)
+        if not p.causal:
+            work *= 2.0  # every (query, key) pair visible
         unit, metric, bound = "TFLOP/s", "prefill TFLOP/s", "mfma"
         desc = f"{name}: B {p.B}, H {p.H}, H_kv {p.H_kv}, N {p.N}, d_qk {p.d_qk}, d_v {p.d_v}, {p.dtype}"
         if win:
@@ -329,9 +338,10 @@ def main():
                     help="profiling aid: run only one part of the step")
     ap.add_argument("--workload", default="step",
                     choices=["step", "prefill_v1", "prefill_v2", "longctx_v1", "tiny_v1", "decode_v2",
-                             "decode_v1", "decode_v2_fp8", "backward_v1", "backward_v2", "copy"],
+                             "decode_v1", "decode_v2_fp8", "backward_v1", "backward_v2", "copy", "copy_lds"],
                     help="step: the whole path (default); otherwise time one workload alone "
-                         "(copy: a plain device copy of 4 GiB, for calibrating HBM byte counters)")
+                         "(copy: a plain device copy of 4 GiB, and copy_lds: a prefill whose key/value bytes "
+                         "are each read once through LDS-DMA loads, for calibrating HBM byte counters)")
     ap.add_argument("--window", type=int, default=0,
                     help="causal sliding window for a single prefill workload (0 = none)")
     args = ap.parse_args()

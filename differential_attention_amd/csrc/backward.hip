@@ -198,9 +198,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc) df[kc] = as_bf16x8(ldg16(d + 8 * hh + 16 * kc));
     }
-    const float lse2 = (br ? p.lse2 : p.lse1)[rowid] * kLog2e;  // log2 units
-    const float dtr = (br ? p.dt2 : p.dt1)[rowid];
+    // dS = w P (G - D) with w = 1 or -lambda, formed as P' (G' - D'): |w| folded
+    // into the exponent (P' = 2^(s - lse + log2|w|); w = 0 gives 2^-inf = 0)
+    // and the sign of w into dy (an exact bf16 sign flip, so G' = sign(w) G)
+    // and D' = sign(w) D: two vector operations per score instead of three
     const float w = br ? -p.lambda[h] : 1.0f;
+    const bool wneg = w < 0.0f;
+    if (wneg) {
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) {
+            uint4 x = __builtin_bit_cast(uint4, df[kc]);
+            x.x ^= 0x80008000u;
+            x.y ^= 0x80008000u;
+            x.z ^= 0x80008000u;
+            x.w ^= 0x80008000u;
+            df[kc] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+    const float lse2 = (br ? p.lse2 : p.lse1)[rowid] * kLog2e - log2f(fabsf(w));  // log2 units, |w| folded
+    const float dtr = wneg ? -(br ? p.dt2 : p.dt1)[rowid] : (br ? p.dt2 : p.dt1)[rowid];
 
     const __bf16 *kb1 = p.k1 + b * p.sk1[0] + g * p.sk1[1];
     const __bf16 *kb2 = p.k2 + b * p.sk2[0] + g * p.sk2[1];
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
                 if (key_of_reg(r) >= lim || key_of_reg(r) < lo) pr[r] = 0.0f;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds[r] = w * pr[r] * (gq[r] - dtr);
+        for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (gq[r] - dtr);
         bf16x8 pb[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
