@@ -53,8 +53,10 @@ def prefill_backward(q1, q2, k1, k2, v, lam, dout, *, depth: int, causal: bool, 
     gradient of the output). Shapes as oracle.prefill; dout [B, H, N, d_v].
     Returns dq1, dq2 [B, H, N, d_qk]; dk1, dk2 [B, H_kv, N, d_qk];
     dv [B, H_kv, N, d_v]; dlambda [H]; dgamma [H, d_v] (zeros without norm);
-    and the forward's per-branch normalised outputs o1, o2 [B, H, N, d_v] and
-    natural-log log-sum-exp of the scaled scores lse1, lse2 [B, H, N]."""
+    the forward's per-branch normalised outputs o1, o2 [B, H, N, d_v] and
+    natural-log log-sum-exp of the scaled scores lse1, lse2 [B, H, N]; and dy
+    [B, H, N, d_v], the gradient at y = O_1 - lambda O_2 (dout itself without
+    a norm), whose products with O_2 dlambda sums."""
     f = lambda a: np.asarray(a, np.float64)
     q1, q2, k1, k2, v, dout = (f(x) for x in (q1, q2, k1, k2, v, dout))
     lam = f(lam).reshape(-1)
@@ -80,6 +82,7 @@ def prefill_backward(q1, q2, k1, k2, v, lam, dout, *, depth: int, causal: bool, 
     out["dgamma"] = np.zeros((H, dv_))
     out["o1"] = np.zeros((B, H, N, dv_))
     out["o2"] = np.zeros((B, H, N, dv_))
+    out["dy"] = np.zeros((B, H, N, dv_))
     out["lse1"] = np.zeros((B, H, N))
     out["lse2"] = np.zeros((B, H, N))
 
@@ -120,6 +123,7 @@ def prefill_backward(q1, q2, k1, k2, v, lam, dout, *, depth: int, causal: bool, 
                 dy = r * gd - y * r ** 3 / dv_ * (gd * y).sum(axis=1, keepdims=True)
             else:
                 dy = dz
+            out["dy"][b, h] = dy
             out["dlambda"][h] += -(dy * o2).sum()
             do1, do2 = dy, -lam[h] * dy
             out["dv"][b, kv] += a1.T @ do1 + a2.T @ do2
