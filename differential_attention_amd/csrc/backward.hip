@@ -762,17 +762,62 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             step(base, sb, qb, lamh, mask);
         }
     };
-    if (total > 0) issue_tile(0, st0);
-    for (int x = 0; x < total; x += 2) {
-        wait_vmem_all();
-        __syncthreads();
-        if (x + 1 < total) issue_tile(x + 1, st1);
-        tile_body(st0, x);
-        if (x + 1 >= total) break;
-        wait_vmem_all();
-        __syncthreads();
-        if (x + 2 < total) issue_tile(x + 2, st0);
-        tile_body(st1, x + 1);
+    if constexpr (DQK == 128 && SHARED_K) {
+        // Three phases, each its own loop: the general body (masks) for the tiles
+        // at the ends of the sweep, and an open body (no mask code) for the tiles
+        // every row of which every wave of the work-group sees in full: below the
+        // ragged end, above the key block's diagonal (causal) and inside every
+        // key's window. A mask test inside one loop splits the step into blocks
+        // the scheduler cannot move work across. Phase boundaries sit at even
+        // steps, so each phase starts in stage 0 with its first tile issued. (The
+        // d_qk 64 kernels and the two-key d_qk 128 kernel run no faster this way,
+        // and the latter spills: they keep one loop.)
+        auto tile_body_open = [&](const unsigned char *base, int x) DA_INLINE {
+            int hg;
+            const int t = tile_of(x, hg);
+            const float lamh = ld_uniform(p.lambda + g * p.group + hg);
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) step(base, sb, t * kBN + 32 * sb, lamh, false);
+        };
+        auto phase = [&](auto body, int x0, int x1) DA_INLINE {
+            for (int x = x0; x < x1; x += 2) {
+                wait_vmem_all();
+                __syncthreads();
+                if (x + 1 < total) issue_tile(x + 1, st1);
+                body(st0, x);
+                if (x + 1 >= x1) break;  // only the last phase can end on an odd step
+                wait_vmem_all();
+                __syncthreads();
+                if (x + 2 < total) issue_tile(x + 2, st0);
+                body(st1, x + 1);
+            }
+        };
+        // open tiles: t in [o_lo, o_hi]
+        const int o_hi0 = p.N / kBN - 1;  // (rows past N: the ragged tile is general)
+        const int o_hi = WIN ? min(o_hi0, (k0 + win) / kBN - 1) : o_hi0;
+        const int o_lo = p.causal ? (k0 + kKB - 1 + kBN - 1) / kBN : tlo;
+        const int t_top = tlo + nt - 1;
+        int xa = max(0, (t_top - o_hi) * p.group), xb = (t_top - o_lo + 1) * p.group;
+        xa = min(total, (xa + 1) & ~1);
+        xb = max(xa, min(total, xb) & ~1);
+        if (o_lo > o_hi) xb = xa;
+        if (total > 0) issue_tile(0, st0);
+        phase(tile_body, 0, xa);
+        phase(tile_body_open, xa, xb);
+        phase(tile_body, xb, total);
+    } else {
+        if (total > 0) issue_tile(0, st0);
+        for (int x = 0; x < total; x += 2) {
+            wait_vmem_all();
+            __syncthreads();
+            if (x + 1 < total) issue_tile(x + 1, st1);
+            tile_body(st0, x);
+            if (x + 1 >= total) break;
+            wait_vmem_all();
+            __syncthreads();
+            if (x + 2 < total) issue_tile(x + 2, st0);
+            tile_body(st1, x + 1);
+        }
     }
 
     if (mykey < p.N) {
