@@ -24,9 +24,12 @@
 //                       rows of one head, 8 waves = 4 row groups x 2 branches;
 //                       per 32-key sub-block S^T = K Q^T, G^T = V dy^T,
 //                       dS^T, dQ^T += K^T dS^T (K^T by transposing LDS reads)
-//  bwd_dkdv_kernel      key-major: a work-group owns 128 keys of one KV head,
-//                       4 waves x 32 keys, both branches per wave, and sweeps
-//                       the query tiles of every head of the group: S = Q K^T,
+//  bwd_dkdv_kernel      key-major: a work-group owns 128 keys of one KV head
+//                       (causal, no window: two mirrored blocks of 128 keys,
+//                       one after the other, so every work-group does about
+//                       the same work), 4 waves x 32 keys, both branches per
+//                       wave, and sweeps the query tiles of every head of
+//                       the group: S = Q K^T,
 //                       G = dy V^T, dV^T += dy^T (P_1 - lambda P_2),
 //                       dK^T += Q^T dS (Q^T and dy^T by transposing reads)
 //  bwd_finalize_kernel  sums the partials per head (fixed order: deterministic)
@@ -417,234 +420,317 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int l32 = lane & 31, hh = lane >> 5;
 
     const int U = p.B * p.H_kv;
-    const int kblk = blockIdx.x / U, u = blockIdx.x - kblk * U;  // key blocks with the most queries first
+    const int item = blockIdx.x / U, u = blockIdx.x - item * U;
     const int b = u / p.H_kv, g = u - b * p.H_kv;
-    const int k0 = kblk * kKB;
-    const int kw0 = k0 + wave * kWM;
-    const int mykey = kw0 + l32;
-    const int key = min(mykey, p.N - 1);
+    // Causal without a window: work-group `item` takes key block `item` (its
+    // query tiles swept from the last down) and then the mirror block
+    // key_blocks - 1 - item (swept from its first tile up). Every work-group
+    // then sweeps about the same number of tiles, so a batch of work-groups
+    // starts and ends together, and at any moment the work-groups of one XCD
+    // read at most two tiles: (T steps in) tile T_last - T going down and
+    // tile T going up, for all of them alike.
+    const int npass = !WIN && p.causal && p.key_blocks - 1 - item != item ? 2 : 1;
+#pragma unroll 1
+    for (int pass = 0; pass < npass; ++pass) {
+        const int kblk = pass ? p.key_blocks - 1 - item : item;
+        const bool asc = pass == 1;
+        if (pass) __syncthreads();  // every wave is done with the first block's stages
+        const int k0 = kblk * kKB;
+        const int kw0 = k0 + wave * kWM;
+        const int mykey = kw0 + l32;
+        const int key = min(mykey, p.N - 1);
 
-    // B operands: the lane's key of K1, K2 and V
-    bf16x8 kf1[KC], kf2[KC], vf[8];
-    {
-        const __bf16 *k1 = p.k1 + b * p.sk1[0] + g * p.sk1[1] + (int64_t)key * p.sk1[2];
-        const __bf16 *k2 = p.k2 + b * p.sk2[0] + g * p.sk2[1] + (int64_t)key * p.sk2[2];
-        const __bf16 *vv = p.v + b * p.sv[0] + g * p.sv[1] + (int64_t)key * p.sv[2];
+        // B operands: the lane's key of K1, K2 and V
+        bf16x8 kf1[KC], kf2[KC], vf[8];
+        {
+            const __bf16 *k1 = p.k1 + b * p.sk1[0] + g * p.sk1[1] + (int64_t)key * p.sk1[2];
+            const __bf16 *k2 = p.k2 + b * p.sk2[0] + g * p.sk2[1] + (int64_t)key * p.sk2[2];
+            const __bf16 *vv = p.v + b * p.sv[0] + g * p.sv[1] + (int64_t)key * p.sv[2];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            kf1[kc] = as_bf16x8(ldg16(k1 + 8 * hh + 16 * kc));
-            kf2[kc] = SHARED_K ? kf1[kc] : as_bf16x8(ldg16(k2 + 8 * hh + 16 * kc));
+            for (int kc = 0; kc < KC; ++kc) {
+                kf1[kc] = as_bf16x8(ldg16(k1 + 8 * hh + 16 * kc));
+                kf2[kc] = SHARED_K ? kf1[kc] : as_bf16x8(ldg16(k2 + 8 * hh + 16 * kc));
+            }
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) vf[kc] = as_bf16x8(ldg16(vv + 8 * hh + 16 * kc));
         }
+
+        // query rows that see some key of the block: q >= k0 (causal) and, with
+        // a window, q <= k0 + kKB - 1 + W - 1
+        const int win = WIN ? p.window : 0;
+        const int qlo = p.causal ? min(k0, p.N) : 0;
+        const int qhi = WIN ? min(p.N, k0 + kKB - 1 + win) : p.N;
+        const int tlo = qlo / kBN;
+        const int nt = qhi > qlo ? (qhi + kBN - 1) / kBN - tlo : 0;  // query tiles per head
+        const int total = nt * p.group;                                // (head, tile) pairs
+        // step x visits query tile tlo + nt - 1 - x / group of head x % group:
+        // tiles from the last down, every head of the group at each tile. The
+        // work-groups running together on one XCD hold the same KV head's key
+        // blocks (the KV unit is the fastest-varying part of the block index, so
+        // with B * H_kv a multiple of 8 a unit's blocks all land on one XCD) and
+        // all need the last tiles, so they read the same tiles at about the same
+        // time and that XCD's L2 serves most of them
+        auto tile_of = [&](int x, int &hg) DA_INLINE {
+            const int tt = x / p.group;
+            hg = x - tt * p.group;
+            return asc ? tlo + tt : tlo + nt - 1 - tt;
+        };
+
+        // With qoff32, a tile wholly inside the sequence is copied by buffer
+        // loads: one descriptor per tensor over this batch, the head and first
+        // row (times the strides) as a scalar offset and one per-lane offset per
+        // tensor; a wave's copies of one tensor are whole 16-row steps apart (the
+        // swizzles' period), so Q1 and Q2 share one lane offset and dy has one.
+        // The tile holding the end of the sequence (rows clamped) and huge
+        // strides take the general form.
+        static_assert((kQBytes / 1024) % NW == 0 && (kDBytes / 1024) % NW == 0, "copy i reads one tensor, fixed by i");
+        constexpr int QPB = kQBytes / 1024 / NW;        // a wave's copies per Q tile
+        constexpr int QRows = NW * kRowsPerQBlock;      // rows between them
+        constexpr int DRows = NW * 4;                   // rows between a wave's dy copies
+        static_assert(QRows % 16 == 0 && DRows % 16 == 0, "copy row steps must keep the swizzles");
+        uint32_t qoff, doff;
+        {
+            const int qr = wave * kRowsPerQBlock + lane / kQCh;
+            qoff = 2u * (uint32_t)(qr * p.sq1[2] + 8 * ((lane % kQCh) ^ bk_swz<DQK>(qr)));
+            const int dr = wave * 4 + (lane >> 4);
+            doff = 2u * (uint32_t)(dr * kDV + 8 * ((lane & 15) ^ bv_swz(dr)));
+        }
+        // raw buffer descriptors (stride 0, 32-bit data format: dword 3 = 0x00020000)
+        const __amdgpu_buffer_rsrc_t rq1 =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(p.q1 + b * p.sq1[0]), (short)0, 0x7fffffff, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rq2 =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(p.q2 + b * p.sq2[0]), (short)0, 0x7fffffff, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.dy + (int64_t)b * p.H * p.N * kDV), (short)0, 0x7fffffff, 0x00020000);
+        const float *stat_arr = wave == 0 ? p.lse1 : wave == 1 ? p.lse2 : wave == 2 ? p.dt1 : p.dt2;
+        const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(stat_arr + (int64_t)b * p.H * p.N), (short)0, 0x7fffffff, 0x00020000);
+
+        auto issue_tile = [&](int x, unsigned char *base) DA_INLINE {
+            int hg;
+            const int t = tile_of(x, hg);
+            const int h = g * p.group + hg;
+            const int r0 = t * kBN;
+            if (p.qoff32 && r0 + kBN <= p.N) {
+                const int hs = __builtin_amdgcn_readfirstlane(h), rs = __builtin_amdgcn_readfirstlane(r0);
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) vf[kc] = as_bf16x8(ldg16(vv + 8 * hh + 16 * kc));
-    }
-
-    // query rows that see some key of the block: q >= k0 (causal) and, with
-    // a window, q <= k0 + kKB - 1 + W - 1
-    const int win = WIN ? p.window : 0;
-    const int qlo = p.causal ? min(k0, p.N) : 0;
-    const int qhi = WIN ? min(p.N, k0 + kKB - 1 + win) : p.N;
-    const int tlo = qlo / kBN;
-    const int nt = qhi > qlo ? (qhi + kBN - 1) / kBN - tlo : 0;  // query tiles per head
-    const int total = nt * p.group;                                // (head, tile) pairs
-    // step x visits query tile tlo + nt - 1 - x / group of head x % group:
-    // tiles from the last down, every head of the group at each tile. The
-    // work-groups running together on one XCD hold the same KV head's key
-    // blocks (the KV unit is the fastest-varying part of the block index, so
-    // with B * H_kv a multiple of 8 a unit's blocks all land on one XCD) and
-    // all need the last tiles, so they read the same tiles at about the same
-    // time and that XCD's L2 serves most of them
-    auto tile_of = [&](int x, int &hg) DA_INLINE {
-        const int tt = x / p.group;
-        hg = x - tt * p.group;
-        return tlo + nt - 1 - tt;
-    };
-
-    // With qoff32, a tile wholly inside the sequence is copied by buffer
-    // loads: one descriptor per tensor over this batch, the head and first
-    // row (times the strides) as a scalar offset and one per-lane offset per
-    // tensor; a wave's copies of one tensor are whole 16-row steps apart (the
-    // swizzles' period), so Q1 and Q2 share one lane offset and dy has one.
-    // The tile holding the end of the sequence (rows clamped) and huge
-    // strides take the general form.
-    static_assert((kQBytes / 1024) % NW == 0 && (kDBytes / 1024) % NW == 0, "copy i reads one tensor, fixed by i");
-    constexpr int QPB = kQBytes / 1024 / NW;        // a wave's copies per Q tile
-    constexpr int QRows = NW * kRowsPerQBlock;      // rows between them
-    constexpr int DRows = NW * 4;                   // rows between a wave's dy copies
-    static_assert(QRows % 16 == 0 && DRows % 16 == 0, "copy row steps must keep the swizzles");
-    uint32_t qoff, doff;
-    {
-        const int qr = wave * kRowsPerQBlock + lane / kQCh;
-        qoff = 2u * (uint32_t)(qr * p.sq1[2] + 8 * ((lane % kQCh) ^ bk_swz<DQK>(qr)));
-        const int dr = wave * 4 + (lane >> 4);
-        doff = 2u * (uint32_t)(dr * kDV + 8 * ((lane & 15) ^ bv_swz(dr)));
-    }
-    // raw buffer descriptors (stride 0, 32-bit data format: dword 3 = 0x00020000)
-    const __amdgpu_buffer_rsrc_t rq1 =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(p.q1 + b * p.sq1[0]), (short)0, 0x7fffffff, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rq2 =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(p.q2 + b * p.sq2[0]), (short)0, 0x7fffffff, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.dy + (int64_t)b * p.H * p.N * kDV), (short)0, 0x7fffffff, 0x00020000);
-    const float *stat_arr = wave == 0 ? p.lse1 : wave == 1 ? p.lse2 : wave == 2 ? p.dt1 : p.dt2;
-    const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(stat_arr + (int64_t)b * p.H * p.N), (short)0, 0x7fffffff, 0x00020000);
-
-    auto issue_tile = [&](int x, unsigned char *base) DA_INLINE {
-        int hg;
-        const int t = tile_of(x, hg);
-        const int h = g * p.group + hg;
-        const int r0 = t * kBN;
-        if (p.qoff32 && r0 + kBN <= p.N) {
-            const int hs = __builtin_amdgcn_readfirstlane(h), rs = __builtin_amdgcn_readfirstlane(r0);
-#pragma unroll
-            for (int i = 0; i < kBlocks / NW; ++i) {
-                const int blk = wave + NW * i;
-                if (i < 2 * QPB) {
-                    const int j = i % QPB;
-                    const uint32_t so = 2u * (uint32_t)(hs * p.sq1[1] + (rs + j * QRows) * p.sq1[2]);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(i < QPB ? rq1 : rq2, (lds_void *)(base + blk * 1024), 16,
-                                                             qoff, so, 0, 0);
+                for (int i = 0; i < kBlocks / NW; ++i) {
+                    const int blk = wave + NW * i;
+                    if (i < 2 * QPB) {
+                        const int j = i % QPB;
+                        const uint32_t so = 2u * (uint32_t)(hs * p.sq1[1] + (rs + j * QRows) * p.sq1[2]);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < QPB ? rq1 : rq2, (lds_void *)(base + blk * 1024),
+                                                                 16, qoff, so, 0, 0);
+                    } else {
+                        const int j = i - 2 * QPB;
+                        const uint32_t so = 2u * (uint32_t)((hs * p.N + rs + j * DRows) * kDV);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rdy, (lds_void *)(base + blk * 1024), 16, doff, so,
+                                                                 0, 0);
+                    }
+                }
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rst, (lds_void *)(base + kBlocks * 1024 + wave * 256), 4,
+                                                         4u * (uint32_t)lane, 4u * (uint32_t)(hs * p.N + rs), 0, 0);
+                return;
+            }
+            const __bf16 *qb1 = p.q1 + b * p.sq1[0] + h * p.sq1[1];
+            const __bf16 *qb2 = p.q2 + b * p.sq2[0] + h * p.sq2[1];
+            const __bf16 *db = p.dy + ((int64_t)b * p.H + h) * p.N * kDV;
+            for (int blk = wave; blk < kBlocks; blk += NW) {
+                if (blk < kQBlocks) {
+                    const int qt = blk / (kQBytes / 1024);
+                    const int qbk = blk % (kQBytes / 1024);
+                    const int r = qbk * kRowsPerQBlock + lane / kQCh;
+                    const int col = 8 * ((lane % kQCh) ^ bk_swz<DQK>(r));
+                    const int q = min(r0 + r, p.N - 1);
+                    const __bf16 *src = (qt ? qb2 + (int64_t)q * p.sq2[2] : qb1 + (int64_t)q * p.sq1[2]) + col;
+                    __builtin_amdgcn_global_load_lds(src, (lds_void *)(base + blk * 1024), 16, 0, 0);
                 } else {
-                    const int j = i - 2 * QPB;
-                    const uint32_t so = 2u * (uint32_t)((hs * p.N + rs + j * DRows) * kDV);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdy, (lds_void *)(base + blk * 1024), 16, doff, so, 0, 0);
+                    const int dbk = blk - kQBlocks;
+                    const int r = dbk * 4 + (lane >> 4);
+                    const int col = 8 * ((lane & 15) ^ bv_swz(r));
+                    const int q = min(r0 + r, p.N - 1);
+                    __builtin_amdgcn_global_load_lds(db + (int64_t)q * kDV + col, (lds_void *)(base + blk * 1024),
+                                                     16, 0, 0);
                 }
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rst, (lds_void *)(base + kBlocks * 1024 + wave * 256), 4,
-                                                     4u * (uint32_t)lane, 4u * (uint32_t)(hs * p.N + rs), 0, 0);
-            return;
-        }
-        const __bf16 *qb1 = p.q1 + b * p.sq1[0] + h * p.sq1[1];
-        const __bf16 *qb2 = p.q2 + b * p.sq2[0] + h * p.sq2[1];
-        const __bf16 *db = p.dy + ((int64_t)b * p.H + h) * p.N * kDV;
-        for (int blk = wave; blk < kBlocks; blk += NW) {
-            if (blk < kQBlocks) {
-                const int qt = blk / (kQBytes / 1024);
-                const int qbk = blk % (kQBytes / 1024);
-                const int r = qbk * kRowsPerQBlock + lane / kQCh;
-                const int col = 8 * ((lane % kQCh) ^ bk_swz<DQK>(r));
-                const int q = min(r0 + r, p.N - 1);
-                const __bf16 *src = (qt ? qb2 + (int64_t)q * p.sq2[2] : qb1 + (int64_t)q * p.sq1[2]) + col;
-                __builtin_amdgcn_global_load_lds(src, (lds_void *)(base + blk * 1024), 16, 0, 0);
-            } else {
-                const int dbk = blk - kQBlocks;
-                const int r = dbk * 4 + (lane >> 4);
-                const int col = 8 * ((lane & 15) ^ bv_swz(r));
-                const int q = min(r0 + r, p.N - 1);
-                __builtin_amdgcn_global_load_lds(db + (int64_t)q * kDV + col, (lds_void *)(base + blk * 1024), 16, 0,
-                                                 0);
+            // statistics: wave w loads array w (lse_1, lse_2, dt_1, dt_2), lane = row
+            {
+                const int q = min(r0 + lane, p.N - 1);
+                const int64_t rid = ((int64_t)b * p.H + h) * p.N + q;
+                const float *src = wave == 0 ? p.lse1 : wave == 1 ? p.lse2 : wave == 2 ? p.dt1 : p.dt2;
+                __builtin_amdgcn_global_load_lds(src + rid, (lds_void *)(base + kBlocks * 1024 + wave * 256), 4, 0, 0);
             }
-        }
-        // statistics: wave w loads array w (lse_1, lse_2, dt_1, dt_2), lane = row
-        {
-            const int q = min(r0 + lane, p.N - 1);
-            const int64_t rid = ((int64_t)b * p.H + h) * p.N + q;
-            const float *src = wave == 0 ? p.lse1 : wave == 1 ? p.lse2 : wave == 2 ? p.dt1 : p.dt2;
-            __builtin_amdgcn_global_load_lds(src + rid, (lds_void *)(base + kBlocks * 1024 + wave * 256), 4, 0, 0);
-        }
-    };
+        };
 
-    f32x16 dva[4], dk1a[DQK / 32], dk2a[DQK / 32];
+        f32x16 dva[4], dk1a[DQK / 32], dk2a[DQK / 32];
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) dva[dc] = f32x16{};
+        for (int dc = 0; dc < 4; ++dc) dva[dc] = f32x16{};
 #pragma unroll
-    for (int dc = 0; dc < DQK / 32; ++dc) {
-        dk1a[dc] = f32x16{};
-        dk2a[dc] = f32x16{};
-    }
-    const int qrow = perm_key(l32);
+        for (int dc = 0; dc < DQK / 32; ++dc) {
+            dk1a[dc] = f32x16{};
+            dk2a[dc] = f32x16{};
+        }
+        const int qrow = perm_key(l32);
 
-    // the transposed A operands of one 16-row half t of a sub-block: dy^T for
-    // dV and Q1^T, Q2^T for dK, each 32 columns wide. Read in one batch ahead
-    // of the products (one wave per SIMD: a read issued just before its
-    // product would expose its whole latency to every product).
-    constexpr int KD = DQK / 32;
-    auto read_tr = [&](const unsigned char *base, int sb, int t, bf16x8 *fv, bf16x8 *fk1, bf16x8 *fk2) DA_INLINE {
-        const unsigned char *t1 = base, *t2 = base + kQBytes, *td = base + 2 * kQBytes;
+        // the transposed A operands of one 16-row half t of a sub-block: dy^T for
+        // dV and Q1^T, Q2^T for dK, each 32 columns wide. Read in one batch ahead
+        // of the products (one wave per SIMD: a read issued just before its
+        // product would expose its whole latency to every product).
+        constexpr int KD = DQK / 32;
+        auto read_tr = [&](const unsigned char *base, int sb, int t, bf16x8 *fv, bf16x8 *fk1, bf16x8 *fk2) DA_INLINE {
+            const unsigned char *t1 = base, *t2 = base + kQBytes, *td = base + 2 * kQBytes;
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) fv[dc] = tr_frag(td, lane, 256, BSwzV(), sb, t, dc);
+            for (int dc = 0; dc < 4; ++dc) fv[dc] = tr_frag(td, lane, 256, BSwzV(), sb, t, dc);
 #pragma unroll
-        for (int dc = 0; dc < KD; ++dc) {
-            fk1[dc] = tr_frag(t1, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc);
-            fk2[dc] = tr_frag(t2, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc);
-        }
-    };
-    auto products = [&](bf16x8 wbt, bf16x8 s1t, bf16x8 s2t, const bf16x8 *fv, const bf16x8 *fk1,
-                        const bf16x8 *fk2) DA_INLINE {
+            for (int dc = 0; dc < KD; ++dc) {
+                fk1[dc] = tr_frag(t1, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc);
+                fk2[dc] = tr_frag(t2, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc);
+            }
+        };
+        auto products = [&](bf16x8 wbt, bf16x8 s1t, bf16x8 s2t, const bf16x8 *fv, const bf16x8 *fk1,
+                            const bf16x8 *fk2) DA_INLINE {
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) dva[dc] = mfma32(fv[dc], wbt, dva[dc]);
+            for (int dc = 0; dc < 4; ++dc) dva[dc] = mfma32(fv[dc], wbt, dva[dc]);
 #pragma unroll
-        for (int dc = 0; dc < KD; ++dc) {
-            dk1a[dc] = mfma32(fk1[dc], s1t, dk1a[dc]);
-            if (SHARED_K)
-                dk1a[dc] = mfma32(fk2[dc], s2t, dk1a[dc]);
-            else
-                dk2a[dc] = mfma32(fk2[dc], s2t, dk2a[dc]);
-        }
-    };
+            for (int dc = 0; dc < KD; ++dc) {
+                dk1a[dc] = mfma32(fk1[dc], s1t, dk1a[dc]);
+                if (SHARED_K)
+                    dk1a[dc] = mfma32(fk2[dc], s2t, dk1a[dc]);
+                else
+                    dk2a[dc] = mfma32(fk2[dc], s2t, dk2a[dc]);
+            }
+        };
 
-    // one 32-row query sub-block of the tile at `base` (query rows qb .. qb+31)
-    auto step = [&](const unsigned char *base, int sb, int qb, float lamh, bool mask) DA_INLINE {
-        const unsigned char *t1 = base;
-        const unsigned char *t2 = base + kQBytes;
-        const unsigned char *td = base + 2 * kQBytes;
-        const float *stat = (const float *)(base + 2 * kQBytes + kDBytes);
-        const int r0 = 32 * sb + qrow;
-        // the A operands of the three products are read in one batch ahead of
-        // them: with one wave per SIMD nothing else hides an LDS read's latency,
-        // so a read issued just before its product would stall every product
-        bf16x8 a1[KC], a2[KC], ad[8];
+        // one 32-row query sub-block of the tile at `base` (query rows qb .. qb+31)
+        auto step = [&](const unsigned char *base, int sb, int qb, float lamh, bool mask) DA_INLINE {
+            const unsigned char *t1 = base;
+            const unsigned char *t2 = base + kQBytes;
+            const unsigned char *td = base + 2 * kQBytes;
+            const float *stat = (const float *)(base + 2 * kQBytes + kDBytes);
+            const int r0 = 32 * sb + qrow;
+            // the A operands of the three products are read in one batch ahead of
+            // them: with one wave per SIMD nothing else hides an LDS read's latency,
+            // so a read issued just before its product would stall every product
+            bf16x8 a1[KC], a2[KC], ad[8];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            const int off = r0 * (2 * DQK) + 16 * ((2 * kc + hh) ^ bk_swz<DQK>(r0));
-            a1[kc] = as_bf16x8(*(const uint4 *)(t1 + off));
-            a2[kc] = as_bf16x8(*(const uint4 *)(t2 + off));
-        }
+            for (int kc = 0; kc < KC; ++kc) {
+                const int off = r0 * (2 * DQK) + 16 * ((2 * kc + hh) ^ bk_swz<DQK>(r0));
+                a1[kc] = as_bf16x8(*(const uint4 *)(t1 + off));
+                a2[kc] = as_bf16x8(*(const uint4 *)(t2 + off));
+            }
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) ad[kc] = as_bf16x8(*(const uint4 *)(td + r0 * 256 + 16 * ((2 * kc + hh) ^ bv_swz(r0))));
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 s1 = f32x16{}, s2 = f32x16{}, gq = f32x16{};
+            for (int kc = 0; kc < 8; ++kc)
+                ad[kc] = as_bf16x8(*(const uint4 *)(td + r0 * 256 + 16 * ((2 * kc + hh) ^ bv_swz(r0))));
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 s1 = f32x16{}, s2 = f32x16{}, gq = f32x16{};
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            s1 = mfma32(a1[kc], kf1[kc], s1);
-            s2 = mfma32(a2[kc], kf2[kc], s2);
-        }
+            for (int kc = 0; kc < KC; ++kc) {
+                s1 = mfma32(a1[kc], kf1[kc], s1);
+                s2 = mfma32(a2[kc], kf2[kc], s2);
+            }
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) gq = mfma32(ad[kc], vf[kc], gq);
-        if constexpr (DQK == 64) {
-            // d_qk 64: each 16-row half t of the sub-block (registers 8t .. 8t+7)
-            // is finished and its products issued before the next half's
-            // arithmetic, so that arithmetic can run beside those products (4 %
-            // faster on backward_v1; 2 % slower for d_qk 128, which keeps the
-            // whole-sub-block form below)
-            const float *statc = stat;
+            for (int kc = 0; kc < 8; ++kc) gq = mfma32(ad[kc], vf[kc], gq);
+            if constexpr (DQK == 64) {
+                // d_qk 64: each 16-row half t of the sub-block (registers 8t .. 8t+7)
+                // is finished and its products issued before the next half's
+                // arithmetic, so that arithmetic can run beside those products (4 %
+                // faster on backward_v1; 2 % slower for d_qk 128, which keeps the
+                // whole-sub-block form below)
+                const float *statc = stat;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                float p1[8], p2[8], D1[8], D2[8];
+                for (int t = 0; t < 2; ++t) {
+                    float p1[8], p2[8], D1[8], D2[8];
 #pragma unroll
-                for (int r4 = 0; r4 < 2; ++r4) {
-                    const int rr = 32 * sb + key_of_reg(8 * t + 4 * r4) + 8 * hh;  // 4 consecutive rows
-                    const float4 l1 = *(const float4 *)(statc + rr);
-                    const float4 l2 = *(const float4 *)(statc + 64 + rr);
-                    const float4 t1v = *(const float4 *)(statc + 128 + rr);
-                    const float4 t2v = *(const float4 *)(statc + 192 + rr);
+                    for (int r4 = 0; r4 < 2; ++r4) {
+                        const int rr = 32 * sb + key_of_reg(8 * t + 4 * r4) + 8 * hh;  // 4 consecutive rows
+                        const float4 l1 = *(const float4 *)(statc + rr);
+                        const float4 l2 = *(const float4 *)(statc + 64 + rr);
+                        const float4 t1v = *(const float4 *)(statc + 128 + rr);
+                        const float4 t2v = *(const float4 *)(statc + 192 + rr);
+                        const float L1[4] = {l1.x, l1.y, l1.z, l1.w}, L2[4] = {l2.x, l2.y, l2.z, l2.w};
+                        const float T1[4] = {t1v.x, t1v.y, t1v.z, t1v.w}, T2[4] = {t2v.x, t2v.y, t2v.z, t2v.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 4 * r4 + e;
+                            p1[r] = exp2_fast(fmaf(s1[8 * t + r], p.sc_log2, -L1[e] * kLog2e));
+                            p2[r] = exp2_fast(fmaf(s2[8 * t + r], p.sc_log2, -L2[e] * kLog2e));
+                            D1[r] = T1[e];
+                            D2[r] = T2[e];
+                        }
+                    }
+                    if (mask) {
+                        asm volatile("");
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) {
+                            const int q = qb + key_of_reg(8 * t + r) + 8 * hh;
+                            const bool vis = q < p.N && (!p.causal || q >= mykey) && (!WIN || q - mykey < win);
+                            if (!vis) {
+                                p1[r] = 0.0f;
+                                p2[r] = 0.0f;
+                            }
+                        }
+                    }
+                    float pw[8], d1[8], d2[8];
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const float gr = gq[8 * t + r];
+                        pw[r] = p1[r] - lamh * p2[r];
+                        d1[r] = p1[r] * (gr - D1[r]);
+                        d2[r] = -lamh * p2[r] * (gr - D2[r]);
+                    }
+                    auto pack8f = [](const float *x) DA_INLINE {
+                        const bf16x2 a = pack2(x[0], x[1]), c = pack2(x[2], x[3]);
+                        const bf16x2 e = pack2(x[4], x[5]), f = pack2(x[6], x[7]);
+                        return bf16x8{a[0], a[1], c[0], c[1], e[0], e[1], f[0], f[1]};
+                    };
+                    const bf16x8 wbt = pack8f(pw), s1t = pack8f(d1), s2t = pack8f(d2);
+#pragma unroll
+                    for (int dc = 0; dc < 4; ++dc)
+                        dva[dc] = mfma32(tr_frag(td, lane, 256, BSwzV(), sb, t, dc), wbt, dva[dc]);
+#pragma unroll
+                    for (int dc = 0; dc < DQK / 32; ++dc) {
+                        dk1a[dc] = mfma32(tr_frag(t1, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), s1t, dk1a[dc]);
+                        if (SHARED_K)
+                            dk1a[dc] = mfma32(tr_frag(t2, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), s2t, dk1a[dc]);
+                        else
+                            dk2a[dc] = mfma32(tr_frag(t2, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), s2t, dk2a[dc]);
+                    }
+                }
+            } else {
+                // the first half's transposed operands are read now, under the
+                // arithmetic below, and the second half's after it, all before the
+                // products (backward_v2 7 % faster; the d_qk 64 form above keeps
+                // its reads beside each product, where batching was 1.5 % slower)
+                bf16x8 fv0[4], fk10[KD], fk20[KD];
+                read_tr(base, sb, 0, fv0, fk10, fk20);
+                __builtin_amdgcn_sched_barrier(0);
+                // register r holds query row 32 sb + key_of_reg(r) + 8 hh of the tile
+                float p1[16], p2[16], D1[16], D2[16];
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int rr = 32 * sb + key_of_reg(4 * r4) + 8 * hh;  // 4 consecutive rows
+                    const float4 l1 = *(const float4 *)(stat + rr);
+                    const float4 l2 = *(const float4 *)(stat + 64 + rr);
+                    const float4 t1v = *(const float4 *)(stat + 128 + rr);
+                    const float4 t2v = *(const float4 *)(stat + 192 + rr);
                     const float L1[4] = {l1.x, l1.y, l1.z, l1.w}, L2[4] = {l2.x, l2.y, l2.z, l2.w};
                     const float T1[4] = {t1v.x, t1v.y, t1v.z, t1v.w}, T2[4] = {t2v.x, t2v.y, t2v.z, t2v.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * r4 + e;
-                        p1[r] = exp2_fast(fmaf(s1[8 * t + r], p.sc_log2, -L1[e] * kLog2e));
-                        p2[r] = exp2_fast(fmaf(s2[8 * t + r], p.sc_log2, -L2[e] * kLog2e));
+                        p1[r] = exp2_fast(fmaf(s1[r], p.sc_log2, -L1[e] * kLog2e));
+                        p2[r] = exp2_fast(fmaf(s2[r], p.sc_log2, -L2[e] * kLog2e));
                         D1[r] = T1[e];
                         D2[r] = T2[e];
                     }
                 }
                 if (mask) {
+                    // an opaque statement keeps this a branch taken by the few masked
+                    // sub-blocks, instead of per-element selects evaluated for all
                     asm volatile("");
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        const int q = qb + key_of_reg(8 * t + r) + 8 * hh;
+                    for (int r = 0; r < 16; ++r) {
+                        const int q = qb + key_of_reg(r) + 8 * hh;
                         const bool vis = q < p.N && (!p.causal || q >= mykey) && (!WIN || q - mykey < win);
                         if (!vis) {
                             p1[r] = 0.0f;
@@ -652,195 +738,130 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
                         }
                     }
                 }
-                float pw[8], d1[8], d2[8];
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float gr = gq[8 * t + r];
-                    pw[r] = p1[r] - lamh * p2[r];
-                    d1[r] = p1[r] * (gr - D1[r]);
-                    d2[r] = -lamh * p2[r] * (gr - D2[r]);
-                }
-                auto pack8f = [](const float *x) DA_INLINE {
-                    const bf16x2 a = pack2(x[0], x[1]), c = pack2(x[2], x[3]);
-                    const bf16x2 e = pack2(x[4], x[5]), f = pack2(x[6], x[7]);
-                    return bf16x8{a[0], a[1], c[0], c[1], e[0], e[1], f[0], f[1]};
-                };
-                const bf16x8 wbt = pack8f(pw), s1t = pack8f(d1), s2t = pack8f(d2);
-#pragma unroll
-                for (int dc = 0; dc < 4; ++dc) dva[dc] = mfma32(tr_frag(td, lane, 256, BSwzV(), sb, t, dc), wbt, dva[dc]);
-#pragma unroll
-                for (int dc = 0; dc < DQK / 32; ++dc) {
-                    dk1a[dc] = mfma32(tr_frag(t1, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), s1t, dk1a[dc]);
-                    if (SHARED_K)
-                        dk1a[dc] = mfma32(tr_frag(t2, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), s2t, dk1a[dc]);
-                    else
-                        dk2a[dc] = mfma32(tr_frag(t2, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc), s2t, dk2a[dc]);
-                }
-            }
-        } else {
-            // the first half's transposed operands are read now, under the
-            // arithmetic below, and the second half's after it, all before the
-            // products (backward_v2 7 % faster; the d_qk 64 form above keeps
-            // its reads beside each product, where batching was 1.5 % slower)
-            bf16x8 fv0[4], fk10[KD], fk20[KD];
-            read_tr(base, sb, 0, fv0, fk10, fk20);
-            __builtin_amdgcn_sched_barrier(0);
-            // register r holds query row 32 sb + key_of_reg(r) + 8 hh of the tile
-            float p1[16], p2[16], D1[16], D2[16];
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int rr = 32 * sb + key_of_reg(4 * r4) + 8 * hh;  // 4 consecutive rows
-                const float4 l1 = *(const float4 *)(stat + rr);
-                const float4 l2 = *(const float4 *)(stat + 64 + rr);
-                const float4 t1v = *(const float4 *)(stat + 128 + rr);
-                const float4 t2v = *(const float4 *)(stat + 192 + rr);
-                const float L1[4] = {l1.x, l1.y, l1.z, l1.w}, L2[4] = {l2.x, l2.y, l2.z, l2.w};
-                const float T1[4] = {t1v.x, t1v.y, t1v.z, t1v.w}, T2[4] = {t2v.x, t2v.y, t2v.z, t2v.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * r4 + e;
-                    p1[r] = exp2_fast(fmaf(s1[r], p.sc_log2, -L1[e] * kLog2e));
-                    p2[r] = exp2_fast(fmaf(s2[r], p.sc_log2, -L2[e] * kLog2e));
-                    D1[r] = T1[e];
-                    D2[r] = T2[e];
-                }
-            }
-            if (mask) {
-                // an opaque statement keeps this a branch taken by the few masked
-                // sub-blocks, instead of per-element selects evaluated for all
-                asm volatile("");
+                float pw[16], d1[16], d2[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int q = qb + key_of_reg(r) + 8 * hh;
-                    const bool vis = q < p.N && (!p.causal || q >= mykey) && (!WIN || q - mykey < win);
-                    if (!vis) {
-                        p1[r] = 0.0f;
-                        p2[r] = 0.0f;
+                    pw[r] = p1[r] - lamh * p2[r];
+                    d1[r] = p1[r] * (gq[r] - D1[r]);
+                    d2[r] = -lamh * p2[r] * (gq[r] - D2[r]);
+                }
+                auto pack16 = [](const float *x, bf16x8 *out) DA_INLINE {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const bf16x2 a = pack2(x[8 * t + 0], x[8 * t + 1]), c = pack2(x[8 * t + 2], x[8 * t + 3]);
+                        const bf16x2 e = pack2(x[8 * t + 4], x[8 * t + 5]), f = pack2(x[8 * t + 6], x[8 * t + 7]);
+                        out[t] = bf16x8{a[0], a[1], c[0], c[1], e[0], e[1], f[0], f[1]};
                     }
-                }
+                };
+                bf16x8 wb[2], s1b[2], s2b[2];
+                pack16(pw, wb);
+                pack16(d1, s1b);
+                pack16(d2, s2b);
+                bf16x8 fv1[4], fk11[KD], fk21[KD];
+                read_tr(base, sb, 1, fv1, fk11, fk21);
+                __builtin_amdgcn_sched_barrier(0);
+                products(wb[0], s1b[0], s2b[0], fv0, fk10, fk20);
+                products(wb[1], s1b[1], s2b[1], fv1, fk11, fk21);
             }
-            float pw[16], d1[16], d2[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                pw[r] = p1[r] - lamh * p2[r];
-                d1[r] = p1[r] * (gq[r] - D1[r]);
-                d2[r] = -lamh * p2[r] * (gq[r] - D2[r]);
-            }
-            auto pack16 = [](const float *x, bf16x8 *out) DA_INLINE {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const bf16x2 a = pack2(x[8 * t + 0], x[8 * t + 1]), c = pack2(x[8 * t + 2], x[8 * t + 3]);
-                    const bf16x2 e = pack2(x[8 * t + 4], x[8 * t + 5]), f = pack2(x[8 * t + 6], x[8 * t + 7]);
-                    out[t] = bf16x8{a[0], a[1], c[0], c[1], e[0], e[1], f[0], f[1]};
-                }
-            };
-            bf16x8 wb[2], s1b[2], s2b[2];
-            pack16(pw, wb);
-            pack16(d1, s1b);
-            pack16(d2, s2b);
-            bf16x8 fv1[4], fk11[KD], fk21[KD];
-            read_tr(base, sb, 1, fv1, fk11, fk21);
-            __builtin_amdgcn_sched_barrier(0);
-            products(wb[0], s1b[0], s2b[0], fv0, fk10, fk20);
-            products(wb[1], s1b[1], s2b[1], fv1, fk11, fk21);
-        }
-    };
+        };
 
-    auto tile_body = [&](const unsigned char *base, int x) DA_INLINE {
-        int hg;
-        const int t = tile_of(x, hg);
-        const float lamh = ld_uniform(p.lambda + g * p.group + hg);
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const int qb = t * kBN + 32 * sb;  // first query row of the sub-block
-            // wholly invisible to this wave's keys: skip
-            if (qb >= p.N) continue;
-            if (p.causal && qb + 31 < kw0) continue;
-            if (WIN && qb > kw0 + kWM - 1 + win - 1) continue;
-            const bool mask = qb + 31 >= p.N || (p.causal && qb < kw0 + kWM - 1) ||
-                              (WIN && qb + 31 > kw0 + win - 1);
-            step(base, sb, qb, lamh, mask);
-        }
-    };
-    if constexpr (DQK == 128 && SHARED_K) {
-        // Three phases, each its own loop: the general body (masks) for the tiles
-        // at the ends of the sweep, and an open body (no mask code) for the tiles
-        // every row of which every wave of the work-group sees in full: below the
-        // ragged end, above the key block's diagonal (causal) and inside every
-        // key's window. A mask test inside one loop splits the step into blocks
-        // the scheduler cannot move work across. Phase boundaries sit at even
-        // steps, so each phase starts in stage 0 with its first tile issued. (The
-        // d_qk 64 kernels and the two-key d_qk 128 kernel run no faster this way,
-        // and the latter spills: they keep one loop.)
-        auto tile_body_open = [&](const unsigned char *base, int x) DA_INLINE {
+        auto tile_body = [&](const unsigned char *base, int x) DA_INLINE {
             int hg;
             const int t = tile_of(x, hg);
             const float lamh = ld_uniform(p.lambda + g * p.group + hg);
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) step(base, sb, t * kBN + 32 * sb, lamh, false);
+            for (int sb = 0; sb < 2; ++sb) {
+                const int qb = t * kBN + 32 * sb;  // first query row of the sub-block
+                // wholly invisible to this wave's keys: skip
+                if (qb >= p.N) continue;
+                if (p.causal && qb + 31 < kw0) continue;
+                if (WIN && qb > kw0 + kWM - 1 + win - 1) continue;
+                const bool mask = qb + 31 >= p.N || (p.causal && qb < kw0 + kWM - 1) ||
+                                  (WIN && qb + 31 > kw0 + win - 1);
+                step(base, sb, qb, lamh, mask);
+            }
         };
-        auto phase = [&](auto body, int x0, int x1) DA_INLINE {
-            for (int x = x0; x < x1; x += 2) {
+        if constexpr (DQK == 128 && SHARED_K) {
+            // Three phases, each its own loop: the general body (masks) for the tiles
+            // at the ends of the sweep, and an open body (no mask code) for the tiles
+            // every row of which every wave of the work-group sees in full: below the
+            // ragged end, above the key block's diagonal (causal) and inside every
+            // key's window. A mask test inside one loop splits the step into blocks
+            // the scheduler cannot move work across. Phase boundaries sit at even
+            // steps, so each phase starts in stage 0 with its first tile issued. (The
+            // d_qk 64 kernels and the two-key d_qk 128 kernel run no faster this way,
+            // and the latter spills: they keep one loop.)
+            auto tile_body_open = [&](const unsigned char *base, int x) DA_INLINE {
+                int hg;
+                const int t = tile_of(x, hg);
+                const float lamh = ld_uniform(p.lambda + g * p.group + hg);
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) step(base, sb, t * kBN + 32 * sb, lamh, false);
+            };
+            auto phase = [&](auto body, int x0, int x1) DA_INLINE {
+                for (int x = x0; x < x1; x += 2) {
+                    wait_vmem_all();
+                    __syncthreads();
+                    if (x + 1 < total) issue_tile(x + 1, st1);
+                    body(st0, x);
+                    if (x + 1 >= x1) break;  // only the last phase can end on an odd step
+                    wait_vmem_all();
+                    __syncthreads();
+                    if (x + 2 < total) issue_tile(x + 2, st0);
+                    body(st1, x + 1);
+                }
+            };
+            // open tiles: t in [o_lo, o_hi]
+            const int o_hi0 = p.N / kBN - 1;  // (rows past N: the ragged tile is general)
+            const int o_hi = WIN ? min(o_hi0, (k0 + win) / kBN - 1) : o_hi0;
+            const int o_lo = p.causal ? (k0 + kKB - 1 + kBN - 1) / kBN : tlo;
+            const int t_top = tlo + nt - 1;
+            int xa = asc ? max(0, (o_lo - tlo) * p.group) : max(0, (t_top - o_hi) * p.group);
+            int xb = asc ? (o_hi - tlo + 1) * p.group : (t_top - o_lo + 1) * p.group;
+            xa = min(total, (xa + 1) & ~1);
+            xb = max(xa, min(total, xb) & ~1);
+            if (o_lo > o_hi) xb = xa;
+            if (total > 0) issue_tile(0, st0);
+            phase(tile_body, 0, xa);
+            phase(tile_body_open, xa, xb);
+            phase(tile_body, xb, total);
+        } else {
+            if (total > 0) issue_tile(0, st0);
+            for (int x = 0; x < total; x += 2) {
                 wait_vmem_all();
                 __syncthreads();
                 if (x + 1 < total) issue_tile(x + 1, st1);
-                body(st0, x);
-                if (x + 1 >= x1) break;  // only the last phase can end on an odd step
+                tile_body(st0, x);
+                if (x + 1 >= total) break;
                 wait_vmem_all();
                 __syncthreads();
                 if (x + 2 < total) issue_tile(x + 2, st0);
-                body(st1, x + 1);
+                tile_body(st1, x + 1);
             }
-        };
-        // open tiles: t in [o_lo, o_hi]
-        const int o_hi0 = p.N / kBN - 1;  // (rows past N: the ragged tile is general)
-        const int o_hi = WIN ? min(o_hi0, (k0 + win) / kBN - 1) : o_hi0;
-        const int o_lo = p.causal ? (k0 + kKB - 1 + kBN - 1) / kBN : tlo;
-        const int t_top = tlo + nt - 1;
-        int xa = max(0, (t_top - o_hi) * p.group), xb = (t_top - o_lo + 1) * p.group;
-        xa = min(total, (xa + 1) & ~1);
-        xb = max(xa, min(total, xb) & ~1);
-        if (o_lo > o_hi) xb = xa;
-        if (total > 0) issue_tile(0, st0);
-        phase(tile_body, 0, xa);
-        phase(tile_body_open, xa, xb);
-        phase(tile_body, xb, total);
-    } else {
-        if (total > 0) issue_tile(0, st0);
-        for (int x = 0; x < total; x += 2) {
-            wait_vmem_all();
-            __syncthreads();
-            if (x + 1 < total) issue_tile(x + 1, st1);
-            tile_body(st0, x);
-            if (x + 1 >= total) break;
-            wait_vmem_all();
-            __syncthreads();
-            if (x + 2 < total) issue_tile(x + 2, st0);
-            tile_body(st1, x + 1);
         }
-    }
 
-    if (mykey < p.N) {
-        const int64_t kid = ((int64_t)b * p.H_kv + g) * p.N + mykey;
-        float *ov = p.dv + kid * kDV + 4 * hh;
+        if (mykey < p.N) {
+            const int64_t kid = ((int64_t)b * p.H_kv + g) * p.N + mykey;
+            float *ov = p.dv + kid * kDV + 4 * hh;
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc)
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const float4 v4 = {dva[dc][4 * rq], dva[dc][4 * rq + 1], dva[dc][4 * rq + 2], dva[dc][4 * rq + 3]};
-                *(float4 *)(ov + 32 * dc + 8 * rq) = v4;
-            }
-#pragma unroll
-        for (int kk = 0; kk < (SHARED_K ? 1 : 2); ++kk) {
-            float *ok = (kk ? p.dk2 : p.dk1) + kid * DQK + 4 * hh;
-#pragma unroll
-            for (int dc = 0; dc < DQK / 32; ++dc) {
-                const f32x16 a = kk ? dk2a[dc] : dk1a[dc];
+            for (int dc = 0; dc < 4; ++dc)
 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) {
-                    const float4 v4 = {a[4 * rq] * p.scale, a[4 * rq + 1] * p.scale, a[4 * rq + 2] * p.scale,
-                                       a[4 * rq + 3] * p.scale};
-                    *(float4 *)(ok + 32 * dc + 8 * rq) = v4;
+                    const float4 v4 = {dva[dc][4 * rq], dva[dc][4 * rq + 1], dva[dc][4 * rq + 2], dva[dc][4 * rq + 3]};
+                    *(float4 *)(ov + 32 * dc + 8 * rq) = v4;
+                }
+#pragma unroll
+            for (int kk = 0; kk < (SHARED_K ? 1 : 2); ++kk) {
+                float *ok = (kk ? p.dk2 : p.dk1) + kid * DQK + 4 * hh;
+#pragma unroll
+                for (int dc = 0; dc < DQK / 32; ++dc) {
+                    const f32x16 a = kk ? dk2a[dc] : dk1a[dc];
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const float4 v4 = {a[4 * rq] * p.scale, a[4 * rq + 1] * p.scale, a[4 * rq + 2] * p.scale,
+                                           a[4 * rq + 3] * p.scale};
+                        *(float4 *)(ok + 32 * dc + 8 * rq) = v4;
+                    }
                 }
             }
         }
@@ -850,7 +871,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 template <int DQK, bool SHARED_K, bool WIN>
 hipError_t launch_main(const BwdParams &p, hipStream_t stream) {
     const int64_t dq_blocks = (int64_t)p.B * p.H * p.row_blocks;
-    const int64_t kv_blocks = (int64_t)p.B * p.H_kv * p.key_blocks;
+    const int64_t kv_blocks = (int64_t)p.B * p.H_kv * (!WIN && p.causal ? (p.key_blocks + 1) / 2 : p.key_blocks);
     if (dq_blocks > 0x7fffffff || kv_blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dq_kernel<DQK, SHARED_K, WIN>), dim3((int)dq_blocks), dim3(512), 0, stream, p);
     hipError_t e = hipGetLastError();
