@@ -21,7 +21,8 @@
 //                       rowsum(dy o_k) from the rounded dy, and per block of
 //                       64 rows the partial sums of dlambda and dgamma
 //  bwd_dq_kernel        query-major, like the forward: a work-group owns 128
-//                       rows of one head, 8 waves = 4 row groups x 2 branches;
+//                       rows of one head (the heads of one KV group on one
+//                       XCD), 8 waves = 4 row groups x 2 branches;
 //                       per 32-key sub-block S^T = K Q^T, G^T = V dy^T,
 //                       dS^T, dQ^T += K^T dS^T (K^T by transposing LDS reads)
 //  bwd_dkdv_kernel      key-major: a work-group owns 128 keys of one KV head
@@ -59,6 +60,7 @@ struct BwdParams {
     float *dt1, *dt2;  // workspace: rowsum(dy * o_k), [B, H, N]
     float *part;       // workspace: per prep block [dlambda, dgamma[128]]
     int B, H, H_kv, group, N, causal, window, norm, prep_nblk, row_blocks, key_blocks;
+    int xcd_units;  // dQ grid: B * H_kv / 8 when B * H_kv is a multiple of 8, else 0
     int qoff32;  // Q1 and Q2 share their strides and one batch of each spans fewer than 2^31 bytes
     int koff32;  // K1 and K2 share their row stride and each (batch, KV head) slice of K1, K2, V spans < 2^31 bytes
     float scale, sc_log2, eps, one_minus_init;
@@ -180,7 +182,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     const int br = wave & 1, rg = wave >> 1;
 
     const int U = p.B * p.H;
-    const int rank = blockIdx.x / U, u = blockIdx.x - rank * U;
+    int rank, u;
+    if (p.xcd_units) {
+        // work-groups go round-robin over the 8 XCDs: XCD L % 8 takes the
+        // xcd_units KV units L % 8, L % 8 + 8, ..., each with every head of
+        // its group, so the work-groups on one XCD stream the key/value
+        // tiles of few KV heads and its L2 serves them
+        const int L = blockIdx.x, xcd = L & 7, sidx = L >> 3;
+        const int per = p.xcd_units * p.group;
+        rank = sidx / per;
+        const int rest = sidx - rank * per;
+        const int kvu = (rest / p.group) * 8 + xcd;
+        const int hig = rest - (rest / p.group) * p.group;
+        const int bb = kvu / p.H_kv, gg = kvu - bb * p.H_kv;
+        u = bb * p.H + gg * p.group + hig;
+    } else {
+        rank = blockIdx.x / U;
+        u = blockIdx.x - rank * U;
+    }
     const int b = u / p.H, h = u - b * p.H;
     const int rb = p.causal ? p.row_blocks - 1 - rank : rank;  // longest rows first
     const int g = h / p.group;
@@ -963,6 +982,7 @@ hipError_t launch_backward_bf16(const diffattn_backward_args &a, const BackwardP
     p.prep_nblk = (a.N + kBwdPrepRows - 1) / kBwdPrepRows;
     p.row_blocks = (a.N + kBM - 1) / kBM;
     p.key_blocks = (a.N + kKB - 1) / kKB;
+    p.xcd_units = (a.B * a.H_kv) % 8 == 0 ? a.B * a.H_kv / 8 : 0;
     {
         // the buffer-load copies keep every offset inside one batch below 2^31
         // bytes: Q1 and Q2 (equal strides), dy (bf16, [H, N, 128]) and the
