@@ -28,16 +28,12 @@ PLAIN_SOURCES = ["plan.cpp"]    # host code with no HIP dependency
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # per-source device flags:
-#  * decode.hip keeps its MFMA accumulators in ordinary VGPRs (its online-
-#    softmax rescale reads them with VALU ops, which cannot address AGPRs),
-#    avoiding a copy of every accumulator per page slice;
 #  * prefill_bf16.hip is compiled without NaN semantics, so fmaxf needs no
 #    canonicalising v_max per operand in the row-max reductions (about 3 %
 #    faster). Its arithmetic never produces a NaN from finite inputs: masked
 #    scores are -inf, exp2(-inf) = 0, and the rescale never subtracts -inf
 #    from -inf; infinities keep their IEEE meaning.
 SOURCE_FLAGS = {
-    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "prefill_bf16.hip": ["-fno-honor-nans"],
 }
 

@@ -100,6 +100,15 @@ struct DecodeParams {
 };
 
 __device__ __forceinline__ uint4 ldg16(const __bf16 *p) { return *(const uint4 *)p; }
+// 16 bytes of the key/value caches: a non-temporal load (every cache line is
+// read once per call, so none is worth keeping in the caches), which streams
+// about 8 % faster than an ordinary load (a plain read of a large buffer:
+// 6.45 against 6.0 TB/s)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldnt16(const void *p) {
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // first token the query sees: L - W with a window W < L, else 0
 __device__ __forceinline__ int first_token(const DecodeParams &p, int L) {
@@ -287,31 +296,31 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                     const unsigned char *vp = (const unsigned char *)p.vc + (row0 + (lane >> 3)) * kDV + 16 * (lane & 7);
                     if (DQK == 128) {
                         const unsigned char *kp = (const unsigned char *)p.kc + (row0 + n) * DQK + 32 * grp;
-                        S.k[0] = *(const uint4 *)kp;
-                        S.k[1] = *(const uint4 *)(kp + 16);
+                        S.k[0] = ldnt16(kp);
+                        S.k[1] = ldnt16(kp + 16);
                     } else {
                         const int64_t off = (row0 + n) * DQK + 16 * grp;
-                        S.k[0] = *(const uint4 *)((const unsigned char *)p.kc + off);
-                        S.k[1] = *(const uint4 *)((const unsigned char *)p.kc2 + off);
+                        S.k[0] = ldnt16((const unsigned char *)p.kc + off);
+                        S.k[1] = ldnt16((const unsigned char *)p.kc2 + off);
                     }
-                    S.v[0] = *(const uint4 *)vp;
-                    S.v[1] = *(const uint4 *)(vp + 8 * kDV);
+                    S.v[0] = ldnt16(vp);
+                    S.v[1] = ldnt16(vp + 8 * kDV);
                 } else {
                     const __bf16 *vp = p.vc + row0 * kDV + grp * kDV + 8 * n;
                     if (DQK == 128) {
                         const __bf16 *kp = p.kc + (row0 + n) * DQK + 8 * grp;
 #pragma unroll
-                        for (int kc = 0; kc < 4; ++kc) S.k[kc] = ldg16(kp + 32 * kc);
+                        for (int kc = 0; kc < 4; ++kc) S.k[kc] = ldnt16(kp + 32 * kc);
                     } else {
                         const __bf16 *kp1 = p.kc + (row0 + n) * DQK + 8 * grp;
                         const __bf16 *kp2 = p.kc2 + (row0 + n) * DQK + 8 * grp;
-                        S.k[0] = ldg16(kp1);
-                        S.k[1] = ldg16(kp1 + 32);
-                        S.k[2] = ldg16(kp2);
-                        S.k[3] = ldg16(kp2 + 32);
+                        S.k[0] = ldnt16(kp1);
+                        S.k[1] = ldnt16(kp1 + 32);
+                        S.k[2] = ldnt16(kp2);
+                        S.k[3] = ldnt16(kp2 + 32);
                     }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) S.v[i] = ldg16(vp + 4 * i * kDV);
+                    for (int i = 0; i < 4; ++i) S.v[i] = ldnt16(vp + 4 * i * kDV);
                 }
             };
 
