@@ -57,7 +57,8 @@ struct BwdParams {
     const float *lambda, *gamma, *o1, *o2, *lse1, *lse2;
     float *dq1, *dq2, *dk1, *dk2, *dv, *dlambda, *dgamma;
     __bf16 *dy;        // workspace: output gradient after the norm, [B, H, N, 128]
-    float *dt1, *dt2;  // workspace: rowsum(dy * o_k), [B, H, N]
+    float *dt1, *dt2;  // workspace: rowsum(dy * o_1) and sign(lambda) rowsum(dy * o_2), [B, H, N]
+    float *ls1, *ls2;  // workspace: lse_1 log2(e) and lse_2 log2(e) - log2|lambda|, [B, H, N]
     float *part;       // workspace: per prep block [dlambda, dgamma[128]]
     int B, H, H_kv, group, N, causal, window, norm, prep_nblk, row_blocks, key_blocks;
     int xcd_units;  // dQ grid: B * H_kv / 8 when B * H_kv is a multiple of 8, else 0
@@ -125,9 +126,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
         const float f0 = (float)b0, f1 = (float)b1;
         const float t1 = wave_sum(f0 * a0 + f1 * a1);
         const float t2 = wave_sum(f0 * e0 + f1 * e1);
+        // per row, for the score-gradient kernels: the log-sum-exp in log2
+        // units, with |lambda| folded into branch 2's (2^(s - ls2) = |lambda| P_2;
+        // lambda = 0 gives 2^-inf = 0), and branch 2's row sum times sign(lambda)
         if (lane == 0) {
             p.dt1[rowid] = t1;
-            p.dt2[rowid] = t2;
+            p.dt2[rowid] = lam > 0.0f ? t2 : (lam < 0.0f ? -t2 : 0.0f);
+            p.ls1[rowid] = p.lse1[rowid] * kLog2e;
+            p.ls2[rowid] = p.lse2[rowid] * kLog2e - log2f(fabsf(lam));
         }
     }
     red[wave][c0] = pg0;
@@ -237,8 +243,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
             df[kc] = __builtin_bit_cast(bf16x8, x);
         }
     }
-    const float lse2 = (br ? p.lse2 : p.lse1)[rowid] * kLog2e - log2f(fabsf(w));  // log2 units, |w| folded
-    const float dtr = wneg ? -(br ? p.dt2 : p.dt1)[rowid] : (br ? p.dt2 : p.dt1)[rowid];
+    // log2 units, |w| folded (by the prep kernel); D' = sign(w) D, which for
+    // branch 2 (w = -lambda, its row sum stored times sign(lambda)) is minus
+    // the stored value
+    const float lse2 = (br ? p.ls2 : p.ls1)[rowid];
+    const float dtr = br ? -p.dt2[rowid] : p.dt1[rowid];
 
     const __bf16 *kb1 = p.k1 + b * p.sk1[0] + g * p.sk1[1];
     const __bf16 *kb2 = p.k2 + b * p.sk2[0] + g * p.sk2[1];
@@ -521,7 +530,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             __builtin_amdgcn_make_buffer_rsrc((void *)(p.q2 + b * p.sq2[0]), (short)0, 0x7fffffff, 0x00020000);
         const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(p.dy + (int64_t)b * p.H * p.N * kDV), (short)0, 0x7fffffff, 0x00020000);
-        const float *stat_arr = wave == 0 ? p.lse1 : wave == 1 ? p.lse2 : wave == 2 ? p.dt1 : p.dt2;
+        const float *stat_arr = wave == 0 ? p.ls1 : wave == 1 ? p.ls2 : wave == 2 ? p.dt1 : p.dt2;
         const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(stat_arr + (int64_t)b * p.H * p.N), (short)0, 0x7fffffff, 0x00020000);
 
@@ -576,7 +585,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             {
                 const int q = min(r0 + lane, p.N - 1);
                 const int64_t rid = ((int64_t)b * p.H + h) * p.N + q;
-                const float *src = wave == 0 ? p.lse1 : wave == 1 ? p.lse2 : wave == 2 ? p.dt1 : p.dt2;
+                const float *src = wave == 0 ? p.ls1 : wave == 1 ? p.ls2 : wave == 2 ? p.dt1 : p.dt2;
                 __builtin_amdgcn_global_load_lds(src + rid, (lds_void *)(base + kBlocks * 1024 + wave * 256), 4, 0, 0);
             }
         };
@@ -621,7 +630,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         };
 
         // one 32-row query sub-block of the tile at `base` (query rows qb .. qb+31)
-        auto step = [&](const unsigned char *base, int sb, int qb, float lamh, bool mask) DA_INLINE {
+        // sg = -sign(lambda) of the head: with the prep kernel's folding,
+        // P_2 |lambda| = 2^(s_2 - ls2), so the combined weight P_1 - lambda P_2 is
+        // P_1 + sg 2^(s_2 - ls2) and dS_2 = -lambda P_2 (G - D_2) is
+        // 2^(s_2 - ls2) (sg G + sign(lambda) D_2), the last term as stored
+        auto step = [&](const unsigned char *base, int sb, int qb, float sg, bool mask) DA_INLINE {
             const unsigned char *t1 = base;
             const unsigned char *t2 = base + kQBytes;
             const unsigned char *td = base + 2 * kQBytes;
@@ -671,8 +684,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int r = 4 * r4 + e;
-                            p1[r] = exp2_fast(fmaf(s1[8 * t + r], p.sc_log2, -L1[e] * kLog2e));
-                            p2[r] = exp2_fast(fmaf(s2[8 * t + r], p.sc_log2, -L2[e] * kLog2e));
+                            p1[r] = exp2_fast(fmaf(s1[8 * t + r], p.sc_log2, -L1[e]));
+                            p2[r] = exp2_fast(fmaf(s2[8 * t + r], p.sc_log2, -L2[e]));
                             D1[r] = T1[e];
                             D2[r] = T2[e];
                         }
@@ -693,9 +706,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                     for (int r = 0; r < 8; ++r) {
                         const float gr = gq[8 * t + r];
-                        pw[r] = p1[r] - lamh * p2[r];
+                        pw[r] = fmaf(sg, p2[r], p1[r]);
                         d1[r] = p1[r] * (gr - D1[r]);
-                        d2[r] = -lamh * p2[r] * (gr - D2[r]);
+                        d2[r] = p2[r] * fmaf(sg, gr, D2[r]);
                     }
                     auto pack8f = [](const float *x) DA_INLINE {
                         const bf16x2 a = pack2(x[0], x[1]), c = pack2(x[2], x[3]);
@@ -737,8 +750,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * r4 + e;
-                        p1[r] = exp2_fast(fmaf(s1[r], p.sc_log2, -L1[e] * kLog2e));
-                        p2[r] = exp2_fast(fmaf(s2[r], p.sc_log2, -L2[e] * kLog2e));
+                        p1[r] = exp2_fast(fmaf(s1[r], p.sc_log2, -L1[e]));
+                        p2[r] = exp2_fast(fmaf(s2[r], p.sc_log2, -L2[e]));
                         D1[r] = T1[e];
                         D2[r] = T2[e];
                     }
@@ -760,9 +773,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
                 float pw[16], d1[16], d2[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    pw[r] = p1[r] - lamh * p2[r];
+                    pw[r] = fmaf(sg, p2[r], p1[r]);
                     d1[r] = p1[r] * (gq[r] - D1[r]);
-                    d2[r] = -lamh * p2[r] * (gq[r] - D2[r]);
+                    d2[r] = p2[r] * fmaf(sg, gq[r], D2[r]);
                 }
                 auto pack16 = [](const float *x, bf16x8 *out) DA_INLINE {
 #pragma unroll
@@ -788,6 +801,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             int hg;
             const int t = tile_of(x, hg);
             const float lamh = ld_uniform(p.lambda + g * p.group + hg);
+            const float sg = lamh > 0.0f ? -1.0f : (lamh < 0.0f ? 1.0f : 0.0f);
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
                 const int qb = t * kBN + 32 * sb;  // first query row of the sub-block
@@ -797,7 +811,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
                 if (WIN && qb > kw0 + kWM - 1 + win - 1) continue;
                 const bool mask = qb + 31 >= p.N || (p.causal && qb < kw0 + kWM - 1) ||
                                   (WIN && qb + 31 > kw0 + win - 1);
-                step(base, sb, qb, lamh, mask);
+                step(base, sb, qb, sg, mask);
             }
         };
         if constexpr (DQK == 128 && SHARED_K) {
@@ -814,8 +828,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
                 int hg;
                 const int t = tile_of(x, hg);
                 const float lamh = ld_uniform(p.lambda + g * p.group + hg);
+                const float sg = lamh > 0.0f ? -1.0f : (lamh < 0.0f ? 1.0f : 0.0f);
 #pragma unroll
-                for (int sb = 0; sb < 2; ++sb) step(base, sb, t * kBN + 32 * sb, lamh, false);
+                for (int sb = 0; sb < 2; ++sb) step(base, sb, t * kBN + 32 * sb, sg, false);
             };
             auto phase = [&](auto body, int x0, int x1) DA_INLINE {
                 for (int x = x0; x < x1; x += 2) {
@@ -970,6 +985,8 @@ hipError_t launch_backward_bf16(const diffattn_backward_args &a, const BackwardP
     p.dy = (__bf16 *)(ws + plan.off_dy);
     p.dt1 = (float *)(ws + plan.off_dt1);
     p.dt2 = (float *)(ws + plan.off_dt2);
+    p.ls1 = (float *)(ws + plan.off_ls1);
+    p.ls2 = (float *)(ws + plan.off_ls2);
     p.part = (float *)(ws + plan.off_part);
     p.B = a.B;
     p.H = a.H;

@@ -396,6 +396,10 @@ int backward_common(const diffattn_backward_args *a, BackwardPlan *plan, std::st
     off += round256((size_t)plan->rows * 4);
     plan->off_dt2 = off;
     off += round256((size_t)plan->rows * 4);
+    plan->off_ls1 = off;
+    off += round256((size_t)plan->rows * 4);
+    plan->off_ls2 = off;
+    off += round256((size_t)plan->rows * 4);
     plan->off_part = off;
     off += round256((size_t)plan->prep_blocks * (1 + a->d_v) * 4);
     plan->ws_bytes = plan->empty ? 0 : off;

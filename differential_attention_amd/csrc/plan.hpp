@@ -55,7 +55,7 @@ struct BackwardPlan {
     bool empty = false;
     int64_t rows = 0;        // B * H * N
     int64_t prep_blocks = 0; // B * H * ceil(N / kBwdPrepRows)
-    size_t off_dy = 0, off_dt1 = 0, off_dt2 = 0, off_part = 0;
+    size_t off_dy = 0, off_dt1 = 0, off_dt2 = 0, off_ls1 = 0, off_ls2 = 0, off_part = 0;
     size_t ws_bytes = 0;
 };
 

@@ -293,7 +293,7 @@ def test_backward_workspace_sizes(lib):
     a = _backward_args()
     rows = 1 * 4 * 128
     r256 = lambda x: -(-x // 256) * 256
-    want = r256(rows * 128 * 2) + 2 * r256(rows * 4) + r256(1 * 4 * 2 * 129 * 4)  # blocks of 64 rows
+    want = r256(rows * 128 * 2) + 4 * r256(rows * 4) + r256(1 * 4 * 2 * 129 * 4)  # blocks of 64 rows
     assert lib.diffattn_backward_workspace_bytes(ctypes.byref(a)) == want
     assert lib.diffattn_backward_workspace_bytes(ctypes.byref(_backward_args(dtype=da.F32))) == 0
 
