@@ -209,7 +209,24 @@ def single_workload(args, torch, da, W, dev):
         return torch.from_numpy(x).to(dev)
 
     name = args.workload
-    if name == "copy":
+    if name in ("gemm", "gemm_zeros"):
+        # the practical bf16 matrix-core ceiling: a large library GEMM (torch.matmul,
+        # hipBLASLt) on N(0,1) operands; gemm_zeros multiplies all-zero operands, whose
+        # lower switching power lets the engine clock run higher
+        n = args.gemm_n
+        g = torch.Generator(device=dev).manual_seed(5)
+        if name == "gemm":
+            A = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            Bm = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        else:
+            A = torch.zeros((n, n), device=dev, dtype=torch.bfloat16)
+            Bm = torch.zeros((n, n), device=dev, dtype=torch.bfloat16)
+        C = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+        call = lambda: torch.matmul(A, Bm, out=C)
+        work, unit, metric, bound = 2.0 * n ** 3, "TFLOP/s", "bf16 GEMM TFLOP/s (torch.matmul)", "mfma"
+        desc = (f"torch.matmul bf16 {n} x {n} x {n}, "
+                + ("N(0,1) operands" if name == "gemm" else "all-zero operands"))
+    elif name == "copy":
         n = 1 << 31  # 2 Gi bf16 elements = 4 GiB read + 4 GiB written
         src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -338,14 +355,19 @@ def main():
                     help="profiling aid: run only one part of the step")
     ap.add_argument("--workload", default="step",
                     choices=["step", "prefill_v1", "prefill_v2", "longctx_v1", "tiny_v1", "decode_v2",
-                             "decode_v1", "decode_v2_fp8", "backward_v1", "backward_v2", "copy", "copy_lds"],
+                             "decode_v1", "decode_v2_fp8", "backward_v1", "backward_v2", "copy", "copy_lds", "gemm",
+                             "gemm_zeros"],
                     help="step: the whole path (default); otherwise time one workload alone "
                          "(copy: a plain device copy of 4 GiB, and copy_lds: a prefill whose key/value bytes "
-                         "are each read once through LDS-DMA loads, for calibrating HBM byte counters)")
+                         "are each read once through LDS-DMA loads, for calibrating HBM byte counters; gemm and "
+                         "gemm_zeros: an n^3 bf16 library GEMM (n = --gemm-n) on N(0,1) or all-zero operands, the practical "
+                         "matrix-core ceiling)")
+    ap.add_argument("--gemm-n", type=int, default=8192, help="matrix size of the gemm workloads")
     ap.add_argument("--window", type=int, default=0,
                     help="causal sliding window for a single prefill workload (0 = none)")
     args = ap.parse_args()
-    if args.window and args.workload in ("step", "copy", "decode_v2", "decode_v1", "decode_v2_fp8", "tiny_v1"):
+    if args.window and args.workload in ("step", "copy", "gemm", "gemm_zeros", "decode_v2", "decode_v1", "decode_v2_fp8",
+                                         "tiny_v1"):
         ap.error("--window applies to a single prefill workload")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
