@@ -22,9 +22,11 @@
 //                       64 rows the partial sums of dlambda and dgamma
 //  bwd_dq_kernel        query-major, like the forward: a work-group owns 128
 //                       rows of one head (the heads of one KV group on one
-//                       XCD), 8 waves = 4 row groups x 2 branches;
-//                       per 32-key sub-block S^T = K Q^T, G^T = V dy^T,
-//                       dS^T, dQ^T += K^T dS^T (K^T by transposing LDS reads)
+//                       XCD), 4 waves of 32 rows, both branches per wave
+//                       (one wave per SIMD); per 32-key sub-block
+//                       S_k^T = K_k Q_k^T, G^T = V dy^T once for both
+//                       branches, dS_k^T, dQ_k^T += K_k^T dS_k^T (K^T by
+//                       transposing LDS reads; shared keys read once)
 //  bwd_dkdv_kernel      key-major: a work-group owns 128 keys of one KV head
 //                       (causal, no window: two mirrored blocks of 128 keys,
 //                       one after the other, so every work-group does about
@@ -176,16 +178,16 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
 // ---------------------------------------------------------------- dQ
 
 template <int DQK, bool SHARED_K, bool WIN>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     using T = Tile<DQK, SHARED_K>;
     constexpr int KC = DQK / 16;
-    constexpr int NW = 8;
+    constexpr int NW = 4;
     __shared__ __attribute__((aligned(1024))) unsigned char st0[T::kStage];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[T::kStage];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int br = wave & 1, rg = wave >> 1;
+    const int rg = wave;  // row group: both branches of 32 rows in one wave
 
     const int U = p.B * p.H;
     int rank, u;
@@ -215,39 +217,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     const int row = min(myrow, p.N - 1);  // rows past the end compute garbage, never stored
     const int64_t rowid = ((int64_t)b * p.H + h) * p.N + row;
 
-    // B operands: this wave's branch of Q, and dy, for the lane's row
-    bf16x8 qf[KC], df[8];
+    // B operands: both branches of Q, and dy, for the lane's row
+    bf16x8 qf[2][KC], df[8];
     {
-        const __bf16 *q = br ? p.q2 + b * p.sq2[0] + h * p.sq2[1] + (int64_t)row * p.sq2[2]
-                             : p.q1 + b * p.sq1[0] + h * p.sq1[1] + (int64_t)row * p.sq1[2];
+        const __bf16 *q1 = p.q1 + b * p.sq1[0] + h * p.sq1[1] + (int64_t)row * p.sq1[2];
+        const __bf16 *q2 = p.q2 + b * p.sq2[0] + h * p.sq2[1] + (int64_t)row * p.sq2[2];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) qf[kc] = as_bf16x8(ldg16(q + 8 * hh + 16 * kc));
+        for (int kc = 0; kc < KC; ++kc) {
+            qf[0][kc] = as_bf16x8(ldg16(q1 + 8 * hh + 16 * kc));
+            qf[1][kc] = as_bf16x8(ldg16(q2 + 8 * hh + 16 * kc));
+        }
         const __bf16 *d = p.dy + rowid * kDV;
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc) df[kc] = as_bf16x8(ldg16(d + 8 * hh + 16 * kc));
     }
-    // dS = w P (G - D) with w = 1 or -lambda, formed as P' (G' - D'): |w| folded
-    // into the exponent (P' = 2^(s - lse + log2|w|); w = 0 gives 2^-inf = 0)
-    // and the sign of w into dy (an exact bf16 sign flip, so G' = sign(w) G)
-    // and D' = sign(w) D: two vector operations per score instead of three
-    const float w = br ? -p.lambda[h] : 1.0f;
-    const bool wneg = w < 0.0f;
-    if (wneg) {
-#pragma unroll
-        for (int kc = 0; kc < 8; ++kc) {
-            uint4 x = __builtin_bit_cast(uint4, df[kc]);
-            x.x ^= 0x80008000u;
-            x.y ^= 0x80008000u;
-            x.z ^= 0x80008000u;
-            x.w ^= 0x80008000u;
-            df[kc] = __builtin_bit_cast(bf16x8, x);
-        }
-    }
-    // log2 units, |w| folded (by the prep kernel); D' = sign(w) D, which for
-    // branch 2 (w = -lambda, its row sum stored times sign(lambda)) is minus
-    // the stored value
-    const float lse2 = (br ? p.ls2 : p.ls1)[rowid];
-    const float dtr = br ? -p.dt2[rowid] : p.dt1[rowid];
+    // dS_1 = P_1 (G - D_1) and dS_2 = -lambda P_2 (G - D_2), with G = dy V^T
+    // formed once for both branches. With the prep kernel's per-row values
+    // (log2 units: ls1, and ls2 with |lambda| folded, so 2^(s_2 - ls2) =
+    // |lambda| P_2; dt2 = sign(lambda) D_2) the second is
+    // 2^(s_2 - ls2) (sg G + dt2) with sg = -sign(lambda), as in the dK/dV kernel
+    const float lamh = p.lambda[h];
+    const float sg = lamh > 0.0f ? -1.0f : (lamh < 0.0f ? 1.0f : 0.0f);
+    const float ls1 = p.ls1[rowid], ls2 = p.ls2[rowid];
+    const float dt1 = p.dt1[rowid], dt2 = p.dt2[rowid];
 
     const __bf16 *kb1 = p.k1 + b * p.sk1[0] + g * p.sk1[1];
     const __bf16 *kb2 = p.k2 + b * p.sk2[0] + g * p.sk2[1];
@@ -326,27 +318,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
         }
     };
 
-    f32x16 dq[DQK / 32];
+    f32x16 dq[2][DQK / 32];
 #pragma unroll
-    for (int dc = 0; dc < DQK / 32; ++dc) dq[dc] = f32x16{};
+    for (int dc = 0; dc < DQK / 32; ++dc) {
+        dq[0][dc] = f32x16{};
+        dq[1][dc] = f32x16{};
+    }
     const int krow = perm_key(l32);
-    const int kt_off = SHARED_K ? 0 : br * T::kKBytes;
 
     auto step = [&](const unsigned char *base, int sb, bool mask, int lim, int lo) DA_INLINE {
-        const unsigned char *kt = base + kt_off;
+        const unsigned char *kt1 = base;
+        const unsigned char *kt2 = base + (SHARED_K ? 0 : T::kKBytes);
         const unsigned char *vt = base + T::kNK * T::kKBytes;
         const int r0 = 32 * sb + krow;
-        bf16x8 kf[KC];
+        // all key fragments (one set feeds both branches when the keys are
+        // shared), then all value fragments, then each half's transposed key
+        // fragments, read before the products that use them (the reads overlap
+        // instead of each product waiting for its own)
+        constexpr int NKT = SHARED_K ? 1 : 2;
+        bf16x8 kf[NKT][KC];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-            kf[kc] = as_bf16x8(*(const uint4 *)(kt + r0 * (2 * DQK) + 16 * ((2 * kc + hh) ^ bk_swz<DQK>(r0))));
-        // all key fragments, then all value fragments, then each half's
-        // transposed key fragments, read before the products that use them
-        // (the reads overlap instead of each product waiting for its own)
+        for (int j = 0; j < NKT; ++j)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                kf[j][kc] = as_bf16x8(
+                    *(const uint4 *)((j ? kt2 : kt1) + r0 * (2 * DQK) + 16 * ((2 * kc + hh) ^ bk_swz<DQK>(r0))));
         __builtin_amdgcn_sched_barrier(0);
-        f32x16 s = f32x16{};
+        f32x16 s1 = f32x16{}, s2 = f32x16{};
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) s = mfma32(kf[kc], qf[kc], s);
+        for (int kc = 0; kc < KC; ++kc) {
+            s1 = mfma32(kf[0][kc], qf[0][kc], s1);
+            s2 = mfma32(kf[NKT - 1][kc], qf[1][kc], s2);
+        }
         f32x16 gq = f32x16{};
         bf16x8 vf[8];
 #pragma unroll
@@ -354,34 +357,53 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc) gq = mfma32(vf[kc], df[kc], gq);
-        float pr[16], ds[16];
+        float p1[16], p2[16], d1[16], d2[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pr[r] = exp2_fast(fmaf(s[r], p.sc_log2, -lse2));
+        for (int r = 0; r < 16; ++r) {
+            p1[r] = exp2_fast(fmaf(s1[r], p.sc_log2, -ls1));
+            p2[r] = exp2_fast(fmaf(s2[r], p.sc_log2, -ls2));
+        }
         if (mask) {
             // an opaque statement keeps this a branch taken by the few masked
             // sub-blocks, instead of per-element selects evaluated for all
             asm volatile("");
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (key_of_reg(r) >= lim || key_of_reg(r) < lo) pr[r] = 0.0f;
+                if (key_of_reg(r) >= lim || key_of_reg(r) < lo) {
+                    p1[r] = 0.0f;
+                    p2[r] = 0.0f;
+                }
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (gq[r] - dtr);
-        bf16x8 pb[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const bf16x2 a = pack2(ds[8 * t + 0], ds[8 * t + 1]), c = pack2(ds[8 * t + 2], ds[8 * t + 3]);
-            const bf16x2 e = pack2(ds[8 * t + 4], ds[8 * t + 5]), f = pack2(ds[8 * t + 6], ds[8 * t + 7]);
-            pb[t] = bf16x8{a[0], a[1], c[0], c[1], e[0], e[1], f[0], f[1]};
+        for (int r = 0; r < 16; ++r) {
+            d1[r] = p1[r] * (gq[r] - dt1);
+            d2[r] = p2[r] * fmaf(sg, gq[r], dt2);
         }
+        auto pack16 = [](const float *x, bf16x8 *out) DA_INLINE {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bf16x2 a = pack2(x[8 * t + 0], x[8 * t + 1]), c = pack2(x[8 * t + 2], x[8 * t + 3]);
+                const bf16x2 e = pack2(x[8 * t + 4], x[8 * t + 5]), f = pack2(x[8 * t + 6], x[8 * t + 7]);
+                out[t] = bf16x8{a[0], a[1], c[0], c[1], e[0], e[1], f[0], f[1]};
+            }
+        };
+        bf16x8 pb1[2], pb2[2];
+        pack16(d1, pb1);
+        pack16(d2, pb2);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            bf16x8 kq[DQK / 32];
+            bf16x8 kq[NKT][DQK / 32];
 #pragma unroll
-            for (int dc = 0; dc < DQK / 32; ++dc) kq[dc] = tr_frag(kt, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc);
+            for (int j = 0; j < NKT; ++j)
+#pragma unroll
+                for (int dc = 0; dc < DQK / 32; ++dc)
+                    kq[j][dc] = tr_frag(j ? kt2 : kt1, lane, 2 * DQK, BSwzK<DQK>(), sb, t, dc);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int dc = 0; dc < DQK / 32; ++dc) dq[dc] = mfma32(kq[dc], pb[t], dq[dc]);
+            for (int dc = 0; dc < DQK / 32; ++dc) {
+                dq[0][dc] = mfma32(kq[0][dc], pb1[t], dq[0][dc]);
+                dq[1][dc] = mfma32(kq[NKT - 1][dc], pb2[t], dq[1][dc]);
+            }
         }
     };
 
@@ -414,15 +436,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     }
 
     if (myrow < p.N) {
-        float *o = (br ? p.dq2 : p.dq1) + (((int64_t)b * p.H + h) * p.N + myrow) * DQK + 4 * hh;
 #pragma unroll
-        for (int dc = 0; dc < DQK / 32; ++dc)
+        for (int j = 0; j < 2; ++j) {
+            float *o = (j ? p.dq2 : p.dq1) + (((int64_t)b * p.H + h) * p.N + myrow) * DQK + 4 * hh;
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const float4 v4 = {dq[dc][4 * rq] * p.scale, dq[dc][4 * rq + 1] * p.scale, dq[dc][4 * rq + 2] * p.scale,
-                                   dq[dc][4 * rq + 3] * p.scale};
-                *(float4 *)(o + 32 * dc + 8 * rq) = v4;
-            }
+            for (int dc = 0; dc < DQK / 32; ++dc)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const float4 v4 = {dq[j][dc][4 * rq] * p.scale, dq[j][dc][4 * rq + 1] * p.scale,
+                                       dq[j][dc][4 * rq + 2] * p.scale, dq[j][dc][4 * rq + 3] * p.scale};
+                    *(float4 *)(o + 32 * dc + 8 * rq) = v4;
+                }
+        }
     }
 }
 
@@ -907,7 +932,7 @@ hipError_t launch_main(const BwdParams &p, hipStream_t stream) {
     const int64_t dq_blocks = (int64_t)p.B * p.H * p.row_blocks;
     const int64_t kv_blocks = (int64_t)p.B * p.H_kv * (!WIN && p.causal ? (p.key_blocks + 1) / 2 : p.key_blocks);
     if (dq_blocks > 0x7fffffff || kv_blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, SHARED_K, WIN>), dim3((int)dq_blocks), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, SHARED_K, WIN>), dim3((int)dq_blocks), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, SHARED_K, WIN>), dim3((int)kv_blocks), dim3(256), 0, stream, p);
