@@ -81,3 +81,11 @@ def test_backward_dkdv_holds_one_wave_a_simd(kernels):
     for k in _of(kernels, "bwd_dkdv_kernel<"):
         assert k["vgprs"] + k["agprs"] > 256, k["kernel"]
         assert k["occupancy_waves_per_simd"] == 1, k["kernel"]
+
+
+def test_backward_dq_holds_both_branches_without_spills(kernels):
+    # 4 waves of 32 rows, both branches per wave (VGPRs and AGPRs together):
+    # one wave per SIMD and nothing spilled
+    for k in _of(kernels, "bwd_dq_kernel<"):
+        assert k["scratch_bytes_per_lane"] == 0, k["kernel"]
+        assert k["occupancy_waves_per_simd"] == 1, k["kernel"]
