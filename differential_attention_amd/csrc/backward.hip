@@ -71,25 +71,41 @@ struct BwdParams {
 
 // ---------------------------------------------------------------- prep
 
+// Sums over the 64 lanes of a wave of K independent values at once (the
+// cross-lane steps of the K sums interleave).
+template <int K>
+__device__ __forceinline__ void wave_sums(float (&x)[K]) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+        for (int k = 0; k < K; ++k) x[k] += __shfl_xor(x[k], o, 64);
+}
+
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     // a block of kBwdPrepRows rows of one (batch, head): each wave takes every
-    // 4th row; the block's dlambda and dgamma sums go to one partial record
+    // 4th row, lane l channels 2l and 2l + 1; the block's dlambda and dgamma
+    // sums go to one partial record
     __shared__ float red[4][kDV + 1];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int c0 = lane, c1 = lane + 64;
+    const int c0 = 2 * lane;
     const float lam = p.lambda[h];
     const float c = p.one_minus_init;
-    const float gm0 = p.norm ? c * p.gamma[(int64_t)h * kDV + c0] : 0.0f;
-    const float gm1 = p.norm ? c * p.gamma[(int64_t)h * kDV + c1] : 0.0f;
+    float gm0 = 0.0f, gm1 = 0.0f;
+    if (p.norm) {
+        const float2 gg = *(const float2 *)(p.gamma + (int64_t)h * kDV + c0);
+        gm0 = c * gg.x;
+        gm1 = c * gg.y;
+    }
     float dl = 0.0f, pg0 = 0.0f, pg1 = 0.0f;
     const int iend = min(p.N, (blk + 1) * kBwdPrepRows);
     for (int i = blk * kBwdPrepRows + wave; i < iend; i += 4) {
         const int64_t rowid = ((int64_t)b * p.H + h) * p.N + i;
-        const float a0 = p.o1[rowid * kDV + c0], a1 = p.o1[rowid * kDV + c1];
-        const float e0 = p.o2[rowid * kDV + c0], e1 = p.o2[rowid * kDV + c1];
-        const __bf16 *dz = p.dout + b * p.sdo[0] + h * p.sdo[1] + (int64_t)i * p.sdo[2];
-        const float z0 = (float)dz[c0], z1 = (float)dz[c1];
+        const float2 av = *(const float2 *)(p.o1 + rowid * kDV + c0);
+        const float2 ev = *(const float2 *)(p.o2 + rowid * kDV + c0);
+        const bf16x2 zv = *(const bf16x2 *)(p.dout + b * p.sdo[0] + h * p.sdo[1] + (int64_t)i * p.sdo[2] + c0);
+        const float a0 = av.x, a1 = av.y, e0 = ev.x, e1 = ev.y;
+        const float z0 = (float)zv[0], z1 = (float)zv[1];
         float y0, y1;
         {
 #pragma clang fp contract(off)
@@ -102,44 +118,51 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
             // (r from the mean square of y, resp. u); with gd = c gamma dz:
             //   RMS:   dy = r gd - y r^3 mean(gd y)
             //   group: dy = r (gd - mean(gd)) - u r^3 mean(gd u)
+            float g0 = gm0 * z0, g1 = gm1 * z1;
             if (p.norm == 2) {
-                const float mu = wave_sum(y0 + y1) * (1.0f / kDV);
+                float m[2] = {y0 + y1, g0 + g1};
+                wave_sums(m);
+                const float mu = m[0] * (1.0f / kDV), gmean = m[1] * (1.0f / kDV);
                 y0 -= mu;
                 y1 -= mu;
+                float q[2] = {y0 * y0 + y1 * y1, g0 * y0 + g1 * y1};
+                wave_sums(q);
+                const float r = 1.0f / sqrtf(q[0] * (1.0f / kDV) + p.eps);
+                const float k3 = r * r * r * (1.0f / kDV) * q[1];
+                d0 = r * (g0 - gmean) - y0 * k3;
+                d1 = r * (g1 - gmean) - y1 * k3;
+                pg0 += z0 * y0 * r * c;
+                pg1 += z1 * y1 * r * c;
+            } else {
+                float q[2] = {y0 * y0 + y1 * y1, g0 * y0 + g1 * y1};
+                wave_sums(q);
+                const float r = 1.0f / sqrtf(q[0] * (1.0f / kDV) + p.eps);
+                const float k3 = r * r * r * (1.0f / kDV) * q[1];
+                d0 = r * g0 - y0 * k3;
+                d1 = r * g1 - y1 * k3;
+                pg0 += z0 * y0 * r * c;
+                pg1 += z1 * y1 * r * c;
             }
-            const float r = 1.0f / sqrtf(wave_sum(y0 * y0 + y1 * y1) * (1.0f / kDV) + p.eps);
-            float g0 = gm0 * z0, g1 = gm1 * z1;
-            const float k3 = r * r * r * (1.0f / kDV) * wave_sum(g0 * y0 + g1 * y1);
-            if (p.norm == 2) {
-                const float gmean = wave_sum(g0 + g1) * (1.0f / kDV);
-                g0 -= gmean;
-                g1 -= gmean;
-            }
-            d0 = r * g0 - y0 * k3;
-            d1 = r * g1 - y1 * k3;
-            pg0 += z0 * y0 * r * c;
-            pg1 += z1 * y1 * r * c;
         }
-        dl -= wave_sum(d0 * e0 + d1 * e1);
-        const __bf16 b0 = (__bf16)d0, b1 = (__bf16)d1;
-        p.dy[rowid * kDV + c0] = b0;
-        p.dy[rowid * kDV + c1] = b1;
+        const bf16x2 bd = pack2(d0, d1);
+        *(bf16x2 *)(p.dy + rowid * kDV + c0) = bd;
         // the softmax-backward row sums use the rounded dy the products use
-        const float f0 = (float)b0, f1 = (float)b1;
-        const float t1 = wave_sum(f0 * a0 + f1 * a1);
-        const float t2 = wave_sum(f0 * e0 + f1 * e1);
+        const float f0 = (float)bd[0], f1 = (float)bd[1];
+        float t[3] = {d0 * e0 + d1 * e1, f0 * a0 + f1 * a1, f0 * e0 + f1 * e1};
+        wave_sums(t);
+        dl -= t[0];
         // per row, for the score-gradient kernels: the log-sum-exp in log2
         // units, with |lambda| folded into branch 2's (2^(s - ls2) = |lambda| P_2;
         // lambda = 0 gives 2^-inf = 0), and branch 2's row sum times sign(lambda)
         if (lane == 0) {
-            p.dt1[rowid] = t1;
-            p.dt2[rowid] = lam > 0.0f ? t2 : (lam < 0.0f ? -t2 : 0.0f);
+            p.dt1[rowid] = t[1];
+            p.dt2[rowid] = lam > 0.0f ? t[2] : (lam < 0.0f ? -t[2] : 0.0f);
             p.ls1[rowid] = p.lse1[rowid] * kLog2e;
             p.ls2[rowid] = p.lse2[rowid] * kLog2e - log2f(fabsf(lam));
         }
     }
     red[wave][c0] = pg0;
-    red[wave][c1] = pg1;
+    red[wave][c0 + 1] = pg1;
     if (lane == 0) red[wave][kDV] = dl;
     __syncthreads();
     float *pp = p.part + (((int64_t)b * p.H + h) * p.prep_nblk + blk) * (kDV + 1);
@@ -149,26 +172,34 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     }
 }
 
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
-    // per head: the partial records summed in a fixed order (deterministic);
-    // thread t < 129 owns value t of every record (t = 0: dlambda, else
-    // dgamma[t - 1]) and keeps 8 independent running sums
-    const int h = blockIdx.x, t = threadIdx.x;
-    if (t > kDV) return;
+__global__ __launch_bounds__(512) void bwd_finalize_kernel(BwdParams p) {
+    // per head: the partial records summed in a fixed order (deterministic).
+    // Wave w sums its contiguous share of the records, in record order, lane
+    // l holding values l and 64 + l of each record (value 128 in lane 0;
+    // value 0 is dlambda, value t > 0 dgamma[t - 1]); the 8 wave sums are
+    // then added in wave order.
+    __shared__ float red[8][kDV + 1];
+    const int h = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t n = (int64_t)p.B * p.prep_nblk;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int64_t k = 0;
-    for (; k + 8 <= n; k += 8)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t r = k + e, bb = r / p.prep_nblk, kb = r - bb * p.prep_nblk;
-            acc[e] += p.part[(((int64_t)bb * p.H + h) * p.prep_nblk + kb) * (kDV + 1) + t];
-        }
-    for (; k < n; ++k) {
-        const int64_t bb = k / p.prep_nblk, kb = k - bb * p.prep_nblk;
-        acc[0] += p.part[(((int64_t)bb * p.H + h) * p.prep_nblk + kb) * (kDV + 1) + t];
+    const int64_t r0 = n * wave / 8, r1 = n * (wave + 1) / 8;
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
+#pragma unroll 4
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t bb = r / p.prep_nblk, kb = r - bb * p.prep_nblk;
+        const float *rec = p.part + (((int64_t)bb * p.H + h) * p.prep_nblk + kb) * (kDV + 1);
+        a0 += rec[lane];
+        a1 += rec[64 + lane];
+        if (lane == 0) a2 += rec[kDV];
     }
-    const float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    red[wave][lane] = a0;
+    red[wave][64 + lane] = a1;
+    if (lane == 0) red[wave][kDV] = a2;
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t > kDV) return;
+    float s = red[0][t];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) s += red[w][t];
     if (t == 0)
         p.dlambda[h] = s;
     else if (p.norm)
@@ -1044,7 +1075,7 @@ hipError_t launch_backward_bf16(const diffattn_backward_args &a, const BackwardP
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(p.prep_nblk, a.H, a.B), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_finalize_kernel, dim3(a.H), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_finalize_kernel, dim3(a.H), dim3(512), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.d_qk == 64) return plan.shared_k ? launch_w<64, true>(p, stream) : launch_w<64, false>(p, stream);
