@@ -144,6 +144,21 @@ def test_backward_parity(torch, da, form, N, causal, window):
         assert np.linalg.norm(dg - ref["dgamma"]) <= 1e-2 * np.linalg.norm(ref["dgamma"])
 
 
+@pytest.mark.parametrize("N,window", [(200, 0), (333, 100)])
+def test_backward_d128_separate_keys(torch, da, N, window):
+    # d_qk 128 with two key tensors (the kernels' non-shared d 128 form: each
+    # branch reads its own key and transposed-key fragments)
+    p = W.prefill_v2(seed=40 + N, B=1, H=4, H_kv=2, N=N, causal=True)
+    rng = np.random.default_rng(41 + N)
+    p.k2 = W.f32_to_bf16(rng.standard_normal(p.k1.shape).astype(np.float32))
+    p.shared_k = False
+    say(f"backward V2 shape, separate K1 and K2, N {N} window {window}")
+    _, _, g, ref = _run(torch, da, p, window=window, seed=N)
+    for name in ("dq1", "dq2", "dk1", "dk2", "dv"):
+        _grad_check(g[name].cpu().numpy(), ref[name], name)
+    _dlambda_check(g["dlambda"].cpu().numpy(), ref["dlambda"], _terms_l2(ref))
+
+
 def test_backward_gqa_groups(torch, da):
     # 8 heads over 2 KV heads (4 heads per KV head accumulate into one dK, dV)
     p = W.prefill_v2(seed=5, B=2, H=8, H_kv=2, N=150)
