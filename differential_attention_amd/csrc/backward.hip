@@ -93,9 +93,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     const float c = p.one_minus_init;
     float gm0 = 0.0f, gm1 = 0.0f;
     if (p.norm) {
-        const float2 gg = *(const float2 *)(p.gamma + (int64_t)h * kDV + c0);
-        gm0 = c * gg.x;
-        gm1 = c * gg.y;
+        // two scalar loads: gamma is only required to be 4-byte aligned
+        gm0 = c * p.gamma[(int64_t)h * kDV + c0];
+        gm1 = c * p.gamma[(int64_t)h * kDV + c0 + 1];
     }
     float dl = 0.0f, pg0 = 0.0f, pg1 = 0.0f;
     const int iend = min(p.N, (blk + 1) * kBwdPrepRows);
