@@ -537,7 +537,8 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
             }
         }
     };
-    // The branch-split sweep runs in up to three phases, each its own loop: the general
+    // The branch-split sweep (and the two-branch sweep without a window) runs in up
+    // to three phases, each its own loop: the general
     // body (all masks) for the tiles holding window-start sub-blocks (the
     // first 4 tiles, windowed kernels only), the open body (no mask code at
     // all) through the middle, and the general body again for the last
@@ -566,7 +567,7 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     };
     auto sweep = [&](auto ft) DA_INLINE {
         if (tlo < ntiles) issue_tile(tlo, st0);
-        if constexpr (S::kOn) {
+        if constexpr (S::kOn || !WIN) {
             constexpr int kTail = S::kBM / kBN;  // tiles holding the waves' diagonal sub-blocks
             const int ta = WIN ? min(ntiles, tlo + 4) : tlo;
             const int tb = max(ta, tlo + 2 * ((ntiles - kTail - tlo) / 2));
@@ -574,9 +575,10 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
             phase(ft, tile_body_open, ta, tb);
             phase(ft, tile_body, tb, ntiles);
         } else {
-            // the two-branch kernels run one phase: the second copy of the step
-            // that separate phases need costs them more (register spills) than the
-            // guarded mask branch it saves
+            // the windowed two-branch kernels run one phase: there the second copy
+            // of the step that separate phases need costs more (register spills:
+            // 12-15 % slower) than the guarded mask branch it saves; without a
+            // window the phases gain 2 % (longctx_v1)
             phase(ft, tile_body, tlo, ntiles);
         }
     };
