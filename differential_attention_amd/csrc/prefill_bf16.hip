@@ -131,12 +131,6 @@ __global__ __launch_bounds__(Split<DQK>::kThreads, Split<DQK>::kMinBlocks) void 
     const int wave = tid >> 6;
     const int lane = tid & 63;
     if (tid == 0) redo_flag = 0;  // read only after the sweep's barriers
-    // Waves w and w + 4 share a SIMD. Waves 0-3 issue at a higher priority,
-    // so when both of a SIMD's waves want the matrix core the same one wins
-    // and the other runs its softmax meanwhile, instead of both advancing
-    // at half rate and then leaving the matrix core idle together (V1 about
-    // 1 % faster, V2 unchanged).
-    if (wave < 4) __builtin_amdgcn_s_setprio(1);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int br0 = S::kOn ? (wave & 1) : 0;   // first branch of this wave (0: Q1/K1, 1: Q2/K2)
