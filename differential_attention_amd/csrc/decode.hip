@@ -173,11 +173,13 @@ struct Slice<true> {
     bool ok;
 };
 
-// 4 e4m3 codes (in memory order) -> 4 bf16 values in the same order
+// 4 e4m3 codes (in memory order) -> 4 bf16 values in the same order: one
+// scaled conversion (scale 1) per two codes, exact since every e4m3 value is
+// a bf16 value
 __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);  // bytes 0, 1
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);   // bytes 2, 3
-    return uint2{__builtin_bit_cast(uint32_t, pack2(a[0], a[1])), __builtin_bit_cast(uint32_t, pack2(b[0], b[1]))};
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);  // bytes 0, 1
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);   // bytes 2, 3
+    return uint2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 
 // 8 codes (two words) -> one bf16x8 MFMA operand
